@@ -1,0 +1,273 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workloads 2,5,3,4,1]
+
+A step is one pass of the whole path over one batch: index scores, top-k, page
+table, sparse attention (decode kernel, or the KV-block-major prefill), LSE
+merge.  The headline line is the decode workload at 64K context, batch 8
+(8 KV groups x 8 heads, d_idx 128, top-16 + own block, paged):
+value = decode tokens/s of one MSA layer = batch x steps / time.
+
+Also reported on the same line:
+  roofline      the index-score kernel (dominant: >90% of the step's bytes)
+                against 8 TB/s HBM, from HIP events around every launch in the
+                timed region; traffic from the committed rocprofv3 counter
+                summary when it was taken on the current kernel source
+  cpu_baseline  the CPU oracle on the host cores over the same batch
+  workloads     the other seeded workloads (1M-context decode, ragged decode,
+                prefill chunk, 4K latency case), each timed the same way
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s + index-scan HBM GB/s @64K/1M ctx; prefill sparse-attn TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MAIN = 2
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_decode-64k-b8.json")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc", "index_score.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="2,5,3,4,1",
+                    help="comma list of workload ids; the first is the headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain 1-read/1-write device copy of this size "
+                         "(reference for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
+    return ap.parse_args()
+
+
+def algorithmic(case, sel=None):
+    """Bytes and FLOPs the method itself must move / compute (not the dense work
+    it avoids)."""
+    import numpy as np
+    pos = case.row_pos.cpu().numpy().astype(np.int64)
+    G, d_idx, n_idx, D, H = case.G, case.d_idx, case.n_idx, case.D, case.H
+    kidx = int(((pos + 1) * G * d_idx * 2).sum())                # visible key-index tokens
+    qidx = case.rows * G * n_idx * d_idx * 2
+    score_out = case.rows * G * case.nb * 4
+    out = dict(kidx=kidx, qidx=qidx, score_bytes=kidx + qidx + score_out,
+               index_flops=float(((pos + 1) * G * n_idx * d_idx * 2).sum()))
+    if sel is not None:
+        s = sel.cpu().numpy().astype(np.int64)
+        valid = s >= 0
+        own = (pos // 128)[:, None, None]
+        vis = np.where(s == own, (pos % 128 + 1)[:, None, None], 128)
+        tokens = int((vis * valid).sum())                           # per (row, group)
+        nsel = valid.sum()
+        out["attn_flops"] = 4.0 * D * tokens * case.Hg             # QK^T and PV, per head
+        out["kv_bytes"] = int(nsel) * 128 * D * 2 * 2
+        out["qo_bytes"] = case.rows * H * D * 2 * 2
+        out["part_bytes"] = int(case.rows * H * case.nslot * (D * 2 + 4))
+    return out
+
+
+def run_workload(cfg, steps, warmup, want_events=True):
+    import torch
+    import block_sparse_attention_09_amd as msa
+    import msa_synth
+
+    case = msa_synth.config_case(cfg, device="cuda")
+    d = msa.Dims(G=case.G, Hg=case.Hg, D=case.D, n_idx=case.n_idx, d_idx=case.d_idx, blk=128)
+    scale = 1.0 / math.sqrt(case.D)
+    dev = case.q.device
+    # outputs and workspace allocated once, outside the timed region
+    scores = torch.empty((case.rows, case.G, case.nb), dtype=torch.float32, device=dev)
+    sel = torch.empty((case.rows, case.G, case.nslot), dtype=torch.int32, device=dev)
+    pt = torch.empty_like(sel)
+    o_part = torch.empty((case.rows, case.H, case.nslot, case.D), dtype=torch.bfloat16,
+                         device=dev)
+    lse_part = torch.empty((case.rows, case.H, case.nslot), dtype=torch.float32, device=dev)
+    o = torch.empty((case.rows, case.H, case.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.rows, case.H), dtype=torch.float32, device=dev)
+    ws = None
+    if case.prefill:
+        nbytes = msa.msa_prefill_workspace_size(d, case.rows, case.nslot, case.num_pages)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    names = ["index_score", "topk", "page_table", "attn", "merge"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos, case.nb,
+                            row_req=case.row_req, blk_lo=case.blk_lo, num_reqs=case.num_reqs,
+                            scores=scores)
+        mark(1)
+        msa.msa_topk_blocks(d, scores, case.row_pos, case.k, sel=sel)
+        mark(2)
+        msa.msa_build_page_table(d, sel, case.block_table, row_req=case.row_req, page_table=pt)
+        mark(3)
+        if case.prefill:
+            msa.msa_sparse_attn_prefill(d, case.q, case.k_cache, case.v_cache, sel, pt,
+                                        case.row_pos, case.num_pages, scale, workspace=ws,
+                                        o_part=o_part, lse_part=lse_part)
+        else:
+            msa.msa_sparse_attn_decode(d, case.q, case.k_cache, case.v_cache, sel, pt,
+                                       case.row_pos, scale, o_part=o_part, lse_part=lse_part)
+        mark(4)
+        msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
+        mark(5)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(evs[i] if want_events else None)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
+           for j, n in enumerate(names)}
+    alg = algorithmic(case, sel)
+    return case, dict(total_ms=total_ms, ms_per_step=total_ms / steps, wall_s=wall,
+                      per_call_ms=per, alg=alg, sel=sel.cpu())
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the index-score kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        info = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    if info.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return info.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case):
+    """The oracle, as it stands, on the host cores over the whole headline batch."""
+    import numpy as np
+    import msa_synth
+    import oracle
+    bits = msa_synth.bits
+    args = dict(q_idx=bits(case.q_idx), k_idx=bits(case.k_idx), q=bits(case.q),
+                k_pool=bits(case.k_cache), v_pool=bits(case.v_cache))
+    bt = case.block_table.cpu().numpy()
+    pos = case.row_pos.cpu().numpy()
+    t = time.perf_counter()
+    oracle.decode_path(args["q_idx"], args["k_idx"], args["q"], args["k_pool"], args["v_pool"],
+                       bt, pos, case.k, case.nb, 1.0 / math.sqrt(case.D))
+    dt = time.perf_counter() - t
+    return dict(value=case.rows / dt, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
+                seconds=round(dt, 3),
+                sample=f"whole {case.name} batch ({case.rows} requests x {case.G} groups): "
+                       "index scores, top-k, page table, direct attention; fp64 C oracle")
+
+
+def summarize(cfg, case, r):
+    a = r["alg"]
+    t = r["per_call_ms"]
+    res = dict(workload=case.name, ms_per_step=round(r["ms_per_step"], 4),
+               per_call_us={k: round(v * 1e3, 2) for k, v in t.items()})
+    score_gbps = a["score_bytes"] / (t["index_score"] * 1e-3) / 1e9
+    res["index_score_GBps"] = round(score_gbps, 1)
+    res["index_score_hbm_frac"] = round(score_gbps / HBM_PEAK_GBPS, 4)
+    res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
+                                   ((t["index_score"] + t["topk"]) * 1e-3) / 1e9, 1)
+    if case.prefill:
+        res["attn_tflops_kernel_call"] = round(a["attn_flops"] / (t["attn"] * 1e-3) / 1e12, 2)
+        res["attn_tflops_with_merge"] = round(a["attn_flops"] /
+                                              ((t["attn"] + t["merge"]) * 1e-3) / 1e12, 2)
+        res["attn_mfma_frac_call"] = round(res["attn_tflops_kernel_call"] / BF16_PEAK_TFLOPS, 4)
+        res["attn_flops"] = a["attn_flops"]
+        res["index_tflops"] = round(a["index_flops"] / (t["index_score"] * 1e-3) / 1e12, 2)
+    else:
+        res["decode_tok_s"] = round(case.rows / (r["ms_per_step"] * 1e-3), 1)
+        step_bytes = a["kidx"] + a["qidx"] + a["kv_bytes"] + a["qo_bytes"]
+        res["step_alg_GBps"] = round(step_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1)
+        attn_bytes = a["kv_bytes"] + a["qo_bytes"] // 2 + a["part_bytes"]
+        res["decode_attn_GBps"] = round(attn_bytes / (t["attn"] * 1e-3) / 1e9, 1)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (the MSA path "
+              "here is a single-GPU build; see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_09_amd as msa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    msa.load()
+    order = [int(x) for x in args.workloads.split(",") if x]
+    main_cfg = order[0]
+    results = {}
+    main_case = main_run = None
+    for cfg in order:
+        steps = args.steps if cfg == main_cfg else max(5, min(args.steps, 20))
+        print(f"[bench] workload {cfg}: {steps} steps", file=sys.stderr, flush=True)
+        case, r = run_workload(cfg, steps, args.warmup)
+        results[cfg] = summarize(cfg, case, r)
+        if cfg == main_cfg:
+            main_case, main_run = case, r
+        else:
+            del case
+            torch.cuda.empty_cache()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    m = results[main_cfg]
+    a = main_run["alg"]
+    t_score = main_run["per_call_ms"]["index_score"]
+    achieved = a["score_bytes"] / (t_score * 1e-3) / 1e9
+    roofline = dict(kernel="index_score_stream_kernel", bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                    traffic=traffic_from_profile(), alg_bytes_per_launch=a["score_bytes"],
+                    avg_launch_us=round(t_score * 1e3, 2))
+    cpu = None
+    if not args.no_cpu_baseline and main_case is not None and not main_case.prefill:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(main_case)
+    value = main_case.rows * args.steps / (main_run["total_ms"] * 1e-3)
+    line = dict(
+        metric=METRIC, value=round(value, 1), unit="tok/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=main_case.name, batch=main_case.rows,
+                    context=int(main_case.ctx_len[0]), G=main_case.G, Hg=main_case.Hg,
+                    head_dim=main_case.D, n_idx=main_case.n_idx, d_idx=main_case.d_idx,
+                    top_k=main_case.k, paged=True, parallelism="none (1 GPU)"),
+        index_scan_GBps=m["index_scan_GBps"], roofline=roofline, cpu_baseline=cpu,
+        device=torch.cuda.get_device_name(0),
+        workloads={results[c]["workload"]: results[c] for c in order})
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

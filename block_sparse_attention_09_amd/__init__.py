@@ -1,0 +1,29 @@
+"""libmsa: MiniMax Sparse Attention (MSA) hot path for MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in ``include/msa.h``.  Every step of
+the path runs in libmsa's HIP kernels; this module only marshals torch tensors
+(device memory and streams) into pointers, sizes and strides, and turns status
+codes into exceptions.  There is no CPU fallback: when ``libmsa.so`` is missing
+the first call raises.
+
+Calls (same names and meaning as the C functions):
+    msa_index_score, msa_topk_blocks, msa_build_page_table,
+    msa_sparse_attn_decode, msa_prefill_workspace_size, msa_sparse_attn_prefill,
+    msa_lse_merge, msa_version
+"""
+from .binding import (  # noqa: F401
+    Dims,
+    MSAError,
+    View,
+    lib_path,
+    load,
+    msa_build_page_table,
+    msa_index_score,
+    msa_lse_merge,
+    msa_prefill_workspace_size,
+    msa_sparse_attn_decode,
+    msa_sparse_attn_prefill,
+    msa_topk_blocks,
+    msa_version,
+    view_of,
+)

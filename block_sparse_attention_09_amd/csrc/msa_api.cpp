@@ -1,0 +1,266 @@
+// msa_api.cpp -- the extern "C" boundary of libmsa: argument validation,
+// launch-geometry choice and status reporting.  No call synchronises or
+// allocates; every kernel goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status_t fail(msa_status_t s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+msa_status_t ok() {
+    g_last_error.clear();
+    return MSA_OK;
+}
+
+msa_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, status, ...)                     \
+    do {                                               \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+msa_status_t check_dims(const msa_dims_t *d, bool need_index, bool need_attn) {
+    REQUIRE(d, MSA_ERR_NULL, "dims is NULL");
+    REQUIRE(d->G >= 1, MSA_ERR_INVALID, "G = %d must be >= 1", d->G);
+    REQUIRE(d->blk == msa::kBlk, MSA_ERR_UNSUPPORTED, "blk = %d: only 128-token blocks", d->blk);
+    if (need_index) {
+        REQUIRE(d->n_idx >= 1 && d->n_idx <= 16, MSA_ERR_UNSUPPORTED,
+                "n_idx = %d: supported 1..16", d->n_idx);
+        REQUIRE(d->d_idx == 64 || d->d_idx == 128, MSA_ERR_UNSUPPORTED,
+                "d_idx = %d: supported 64 or 128", d->d_idx);
+    }
+    if (need_attn) {
+        REQUIRE(d->D == 128, MSA_ERR_UNSUPPORTED, "D = %d: only head dimension 128", d->D);
+        REQUIRE(d->Hg == 1 || d->Hg == 2 || d->Hg == 4 || d->Hg == 8 || d->Hg == 16,
+                MSA_ERR_UNSUPPORTED, "Hg = %d: supported 1, 2, 4, 8, 16", d->Hg);
+    }
+    return MSA_OK;
+}
+
+msa_status_t check_view(const msa_view_t &v, const char *name) {
+    REQUIRE(v.base, MSA_ERR_NULL, "%s.base is NULL", name);
+    REQUIRE(aligned(v.base, 16), MSA_ERR_INVALID, "%s.base must be 16-byte aligned", name);
+    REQUIRE(v.page_stride >= 0 && v.group_stride >= 0 && v.token_stride >= 0, MSA_ERR_INVALID,
+            "%s strides must be >= 0", name);
+    REQUIRE(v.page_stride % 8 == 0 && v.group_stride % 8 == 0 && v.token_stride % 8 == 0,
+            MSA_ERR_INVALID, "%s strides must be multiples of 8 elements", name);
+    return MSA_OK;
+}
+
+hipStream_t as_stream(msa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_version(void) { return "libmsa 0.1.0 (gfx950)"; }
+
+const char *msa_last_error(void) { return g_last_error.c_str(); }
+
+const char *msa_status_string(msa_status_t s) {
+    switch (s) {
+        case MSA_OK: return "MSA_OK";
+        case MSA_ERR_NULL: return "MSA_ERR_NULL: a required pointer is NULL";
+        case MSA_ERR_INVALID: return "MSA_ERR_INVALID: invalid size, stride or alignment";
+        case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: shape not supported";
+        case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace too small";
+        case MSA_ERR_HIP: return "MSA_ERR_HIP: HIP launch failed";
+    }
+    return "unknown msa_status_t";
+}
+
+msa_status_t msa_index_score(const msa_dims_t *dims, int32_t rows, const void *q_idx,
+                             msa_view_t k_idx, const int32_t *block_table, int32_t bt_stride,
+                             const int32_t *row_req, const int32_t *row_pos,
+                             const int32_t *blk_lo, int32_t num_reqs, float *scores,
+                             int32_t score_stride, msa_stream_t stream) {
+    msa_status_t st = check_dims(dims, true, false);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
+    REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
+    REQUIRE(num_reqs >= 1, MSA_ERR_INVALID, "num_reqs = %d must be >= 1", num_reqs);
+    if (rows == 0) return ok();
+    REQUIRE(q_idx && block_table && row_pos && scores, MSA_ERR_NULL,
+            "q_idx, block_table, row_pos and scores are required");
+    REQUIRE(aligned(q_idx, 16), MSA_ERR_INVALID, "q_idx must be 16-byte aligned");
+    REQUIRE(aligned(scores, 4) && aligned(block_table, 4) && aligned(row_pos, 4), MSA_ERR_INVALID,
+            "int32/fp32 arrays must be 4-byte aligned");
+    st = check_view(k_idx, "k_idx");
+    if (st != MSA_OK) return st;
+    return hip_status(msa::launch_index_score(*dims, rows, static_cast<const msa::bf16_t *>(q_idx),
+                                              k_idx, block_table, bt_stride, row_req, row_pos,
+                                              blk_lo, num_reqs, scores, score_stride,
+                                              as_stream(stream)),
+                      "msa_index_score");
+}
+
+msa_status_t msa_topk_blocks(const msa_dims_t *dims, int32_t rows, const float *scores,
+                             int32_t score_stride, const int32_t *row_pos, int32_t k,
+                             int32_t *sel, msa_stream_t stream) {
+    msa_status_t st = check_dims(dims, false, false);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    REQUIRE(k >= 0, MSA_ERR_INVALID, "k = %d must be >= 0", k);
+    REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
+    if (rows == 0) return ok();
+    REQUIRE(scores && row_pos && sel, MSA_ERR_NULL, "scores, row_pos and sel are required");
+    return hip_status(msa::launch_topk(rows, dims->G, scores, score_stride, row_pos, k, sel,
+                                       as_stream(stream)),
+                      "msa_topk_blocks");
+}
+
+msa_status_t msa_build_page_table(const msa_dims_t *dims, int32_t rows, const int32_t *sel,
+                                  int32_t nslot, const int32_t *row_req,
+                                  const int32_t *block_table, int32_t bt_stride,
+                                  int32_t *page_table, msa_stream_t stream) {
+    msa_status_t st = check_dims(dims, false, false);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    REQUIRE(nslot >= 1, MSA_ERR_INVALID, "nslot = %d must be >= 1", nslot);
+    REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
+    if (rows == 0) return ok();
+    REQUIRE(sel && block_table && page_table, MSA_ERR_NULL,
+            "sel, block_table and page_table are required");
+    return hip_status(msa::launch_page_table(rows, dims->G, sel, nslot, row_req, block_table,
+                                             bt_stride, page_table, as_stream(stream)),
+                      "msa_build_page_table");
+}
+
+static msa_status_t check_attn(const msa_dims_t *dims, int32_t rows, const void *q,
+                               const msa_view_t &k, const msa_view_t &v, const int32_t *sel,
+                               const int32_t *page_table, int32_t nslot, const int32_t *row_pos,
+                               float sm_scale, const void *o_part, const float *lse_part) {
+    msa_status_t st = check_dims(dims, false, true);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    REQUIRE(nslot >= 1, MSA_ERR_INVALID, "nslot = %d must be >= 1", nslot);
+    REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, MSA_ERR_INVALID,
+            "sm_scale must be finite and > 0");
+    REQUIRE((int64_t)rows * nslot < (int64_t)1 << 31, MSA_ERR_INVALID,
+            "rows * nslot must fit in int32");
+    if (rows == 0) return MSA_OK;
+    REQUIRE(q && sel && page_table && row_pos && o_part && lse_part, MSA_ERR_NULL,
+            "q, sel, page_table, row_pos, o_part and lse_part are required");
+    REQUIRE(aligned(q, 16) && aligned(o_part, 16), MSA_ERR_INVALID,
+            "q and o_part must be 16-byte aligned");
+    st = check_view(k, "k");
+    if (st != MSA_OK) return st;
+    return check_view(v, "v");
+}
+
+static msa::AttnArgs attn_args(const msa_dims_t *d, int32_t rows, const void *q,
+                               const msa_view_t &k, const msa_view_t &v, const int32_t *sel,
+                               const int32_t *pt, int32_t nslot, const int32_t *row_pos,
+                               float sm_scale, void *o_part, float *lse_part) {
+    msa::AttnArgs a;
+    a.rows = rows;
+    a.G = d->G;
+    a.Hg = d->Hg;
+    a.nslot = nslot;
+    a.q = static_cast<const msa::bf16_t *>(q);
+    a.k = static_cast<const msa::bf16_t *>(k.base);
+    a.kps = k.page_stride;
+    a.kgs = k.group_stride;
+    a.kts = k.token_stride;
+    a.v = static_cast<const msa::bf16_t *>(v.base);
+    a.vps = v.page_stride;
+    a.vgs = v.group_stride;
+    a.vts = v.token_stride;
+    a.sel = sel;
+    a.page_table = pt;
+    a.row_pos = row_pos;
+    a.sm_scale = sm_scale;
+    a.o_part = static_cast<msa::bf16_t *>(o_part);
+    a.lse_part = lse_part;
+    return a;
+}
+
+msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const void *q,
+                                    msa_view_t k, msa_view_t v, const int32_t *sel,
+                                    const int32_t *page_table, int32_t nslot,
+                                    const int32_t *row_pos, float sm_scale, void *o_part,
+                                    float *lse_part, msa_stream_t stream) {
+    msa_status_t st = check_attn(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale,
+                                 o_part, lse_part);
+    if (st != MSA_OK) return st;
+    if (rows == 0) return ok();
+    const msa::AttnArgs a =
+        attn_args(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale, o_part, lse_part);
+    return hip_status(msa::launch_attn_decode(a, as_stream(stream)), "msa_sparse_attn_decode");
+}
+
+msa_status_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t rows, int32_t nslot,
+                                        int32_t num_pages, size_t *bytes) {
+    REQUIRE(bytes, MSA_ERR_NULL, "bytes is NULL");
+    msa_status_t st = check_dims(dims, false, true);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0 && nslot >= 1 && num_pages >= 1, MSA_ERR_INVALID,
+            "rows >= 0, nslot >= 1 and num_pages >= 1 are required");
+    *bytes = msa::prefill_workspace_bytes(rows, dims->G, nslot, num_pages);
+    return ok();
+}
+
+msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t rows, const void *q,
+                                     msa_view_t k, msa_view_t v, const int32_t *sel,
+                                     const int32_t *page_table, int32_t nslot,
+                                     const int32_t *row_pos, int32_t num_pages, float sm_scale,
+                                     void *workspace, size_t workspace_bytes, void *o_part,
+                                     float *lse_part, msa_stream_t stream) {
+    msa_status_t st = check_attn(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale,
+                                 o_part, lse_part);
+    if (st != MSA_OK) return st;
+    REQUIRE(num_pages >= 1, MSA_ERR_INVALID, "num_pages = %d must be >= 1", num_pages);
+    REQUIRE((int64_t)dims->G * num_pages < ((int64_t)1 << 31) - 1, MSA_ERR_INVALID,
+            "G * num_pages must fit in int32");
+    if (rows == 0) return ok();
+    const size_t need = msa::prefill_workspace_bytes(rows, dims->G, nslot, num_pages);
+    REQUIRE(workspace, MSA_ERR_NULL, "workspace is NULL");
+    REQUIRE(aligned(workspace, 16), MSA_ERR_INVALID, "workspace must be 16-byte aligned");
+    REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu",
+            workspace_bytes, need);
+    const msa::AttnArgs a =
+        attn_args(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale, o_part, lse_part);
+    return hip_status(msa::launch_attn_prefill(a, num_pages, workspace, as_stream(stream)),
+                      "msa_sparse_attn_prefill");
+}
+
+msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D, const void *o_part,
+                           const float *lse_part, void *o, float *lse, msa_stream_t stream) {
+    REQUIRE(rows >= 0 && H >= 1 && nslot >= 1, MSA_ERR_INVALID,
+            "rows >= 0, H >= 1 and nslot >= 1 are required");
+    REQUIRE(D == 128, MSA_ERR_UNSUPPORTED, "D = %d: only head dimension 128", D);
+    if (rows == 0) return ok();
+    REQUIRE(o_part && lse_part && o, MSA_ERR_NULL, "o_part, lse_part and o are required");
+    REQUIRE(aligned(o_part, 16) && aligned(o, 16), MSA_ERR_INVALID,
+            "o_part and o must be 16-byte aligned");
+    return hip_status(msa::launch_lse_merge(rows, H, nslot, static_cast<const msa::bf16_t *>(o_part),
+                                            lse_part, static_cast<msa::bf16_t *>(o), lse,
+                                            as_stream(stream)),
+                      "msa_lse_merge");
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// msa_internal.h -- device helpers and launcher declarations shared by the
+// libmsa translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa.h"
+
+namespace msa {
+
+constexpr int kBlk = 128;   // tokens per KV block and per cache page
+constexpr int kWave = 64;   // CDNA wavefront
+
+typedef uint16_t bf16_t;                                              // bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));            // MFMA A/B operand
+typedef float f32x4 __attribute__((ext_vector_type(4)));              // 16x16 accumulator
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));           // 16-byte load
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l holds A[l % 16][8 (l / 16) .. +8], B[8 (l / 16) .. +8][l % 16] and
+// D[4 (l / 16) + i][l % 16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) {
+    return v + __shfl_xor(v, mask, kWave);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are validated by the API layer.
+hipError_t launch_index_score(const msa_dims_t &d, int rows, const bf16_t *q_idx,
+                              const msa_view_t &kv, const int32_t *block_table, int bt_stride,
+                              const int32_t *row_req, const int32_t *row_pos,
+                              const int32_t *blk_lo, int num_reqs, float *scores,
+                              int score_stride, hipStream_t stream);
+
+hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
+                       const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream);
+
+hipError_t launch_page_table(int rows, int G, const int32_t *sel, int nslot,
+                             const int32_t *row_req, const int32_t *block_table, int bt_stride,
+                             int32_t *page_table, hipStream_t stream);
+
+struct AttnArgs {
+    int rows, G, Hg, nslot;
+    const bf16_t *q;
+    const bf16_t *k;
+    int64_t kps, kgs, kts;
+    const bf16_t *v;
+    int64_t vps, vgs, vts;
+    const int32_t *sel, *page_table, *row_pos;
+    float sm_scale;
+    bf16_t *o_part;
+    float *lse_part;
+};
+
+hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int rows, int G, int nslot, int num_pages);
+hipError_t launch_attn_prefill(const AttnArgs &a, int num_pages, void *workspace,
+                               hipStream_t stream);
+
+hipError_t launch_lse_merge(int rows, int H, int nslot, const bf16_t *o_part,
+                            const float *lse_part, bf16_t *o, float *lse, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,184 @@
+// topk.hip -- per (row, KV group) top-k block selection and the page-table
+// gather (gfx950).
+//
+// Pages: the score part of MSA picks the most relevant K blocks for each KV
+// group (架构/特性 of "Together AI 解析如何高效服务 MiniMax M3"); each request and
+// group has its own top-k boundary (解码索引评分内核优化); decode builds a page
+// table from the selected blocks with the KV group folded into the batch
+// (将 MSA 与分页注意力集成).
+//
+// Selection = radix select on order-preserving 32-bit keys of the fp32 scores,
+// one workgroup per (row, group): four 8-bit digit passes (LDS histogram, one
+// wave scans it) find the k-th largest key T and how many keys equal to T are
+// still needed; one ordered pass then keeps keys > T plus the lowest-index keys
+// == T (ties go to the lower block index) and compacts them in ascending block
+// order with wave ballots.  The own block is appended last (it is the largest
+// index) and the rest is padded with -1.  Integer decisions on the caller's
+// fp32 scores only, so the result is exact and deterministic.
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+
+// Order-preserving key: larger float -> larger unsigned; -0 and +0 map together.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (f == 0.0f) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix count of `flag` over the workgroup in thread order; returns
+// the prefix for this thread and writes the workgroup total to *total.
+__device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t bal = __ballot(flag);
+    const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[w] = __popcll(bal);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) {
+        const int c = wave_tot[i];
+        before += (i < w) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + in_wave;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *__restrict__ scores,
+                                                           int score_stride,
+                                                           const int32_t *__restrict__ row_pos,
+                                                           int k, int32_t *__restrict__ sel) {
+    __shared__ uint32_t hist[256];
+    __shared__ int wave_tot[kTopkWaves];
+    __shared__ int sh_digit, sh_above;
+
+    const int rg = blockIdx.x;
+    const int r = rg / G;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int own = row_pos[r] / kBlk;
+    const float *s = scores + (int64_t)rg * score_stride;
+    int32_t *out = sel + (int64_t)rg * (k + 1);
+
+    // number of candidates: blocks before own with a score other than -inf
+    int ncand = 0;
+    for (int base = 0; base < own; base += kTopkThreads) {
+        const int b = base + tid;
+        int t;
+        block_excl_count(b < own && s[b] != -INFINITY, wave_tot, &t);
+        ncand += t;
+    }
+
+    uint32_t thresh = 0u;   // keep keys > thresh ...
+    int take_eq = 0;        // ... plus the first take_eq keys == thresh
+    if (k == 0) {
+        thresh = 0xffffffffu;  // keep nothing but the own block
+    } else if (k < ncand) {
+        uint32_t prefix = 0u, pmask = 0u;
+        int remain = k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            hist[tid] = 0u;
+            __syncthreads();
+            for (int b = tid; b < own; b += kTopkThreads) {
+                const float v = s[b];
+                if (v == -INFINITY) continue;
+                const uint32_t key = order_key(v);
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < kWave) {
+                // lane l owns digits 4l .. 4l+3; suffix sums from the top digit down
+                const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+                const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+                const int local = (int)(h0 + h1 + h2 + h3);
+                int incl = local;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const int v = __shfl_down(incl, off, kWave);
+                    incl += (lane + off < kWave) ? v : 0;
+                }
+                int above = incl - local;  // keys in digits owned by higher lanes
+                const int hd[4] = {(int)h0, (int)h1, (int)h2, (int)h3};
+#pragma unroll
+                for (int e = 3; e >= 0; --e) {
+                    if (above < remain && remain <= above + hd[e]) {
+                        sh_digit = 4 * lane + e;
+                        sh_above = above;
+                    }
+                    above += hd[e];
+                }
+            }
+            __syncthreads();
+            prefix |= (uint32_t)sh_digit << shift;
+            pmask |= 255u << shift;
+            remain -= sh_above;
+            __syncthreads();
+        }
+        thresh = prefix;
+        take_eq = remain;
+    }  // else: every candidate is kept (every finite score's key is > 0)
+
+    // ordered pass: keep, compact ascending, append own, pad
+    int n_sel = 0, n_eq = 0;
+    for (int base = 0; base < own; base += kTopkThreads) {
+        const int b = base + tid;
+        uint32_t key = 0u;
+        bool valid = false;
+        if (b < own) {
+            const float v = s[b];
+            valid = v != -INFINITY;
+            key = valid ? order_key(v) : 0u;
+        }
+        const bool is_eq = valid && key == thresh && take_eq > 0;
+        int eq_tot;
+        const int eq_rank = n_eq + block_excl_count(is_eq, wave_tot, &eq_tot);
+        const bool keep = valid && (key > thresh || (is_eq && eq_rank < take_eq));
+        int keep_tot;
+        const int at = n_sel + block_excl_count(keep, wave_tot, &keep_tot);
+        if (keep) out[at] = b;
+        n_sel += keep_tot;
+        n_eq += eq_tot;
+    }
+    for (int i = n_sel + tid; i <= k; i += kTopkThreads) out[i] = (i == n_sel) ? own : -1;
+    (void)lane;
+}
+
+__global__ void page_table_kernel(int64_t n, int G, int nslot, const int32_t *__restrict__ sel,
+                                  const int32_t *__restrict__ row_req,
+                                  const int32_t *__restrict__ block_table, int bt_stride,
+                                  int32_t *__restrict__ pt) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int r = (int)(i / ((int64_t)G * nslot));
+    const int req = row_req ? row_req[r] : r;
+    const int b = sel[i];
+    pt[i] = (b < 0) ? -1 : block_table[(int64_t)req * bt_stride + b];
+}
+
+}  // namespace
+
+hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
+                       const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream) {
+    const int64_t pairs = (int64_t)rows * G;
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)pairs), dim3(kTopkThreads), 0, stream, G,
+                       scores, score_stride, row_pos, k, sel);
+    return hipGetLastError();
+}
+
+hipError_t launch_page_table(int rows, int G, const int32_t *sel, int nslot,
+                             const int32_t *row_req, const int32_t *block_table, int bt_stride,
+                             int32_t *page_table, hipStream_t stream) {
+    const int64_t n = (int64_t)rows * G * nslot;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(page_table_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, n, G,
+                       nslot, sel, row_req, block_table, bt_stride, page_table);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,221 @@
+/*
+ * msa.h -- C ABI of libmsa, the MI355X (gfx950) hot path of MiniMax Sparse
+ * Attention (MSA).
+ *
+ * The method (pages: "Together AI 解析如何高效服务 MiniMax M3" on aihot.news, section
+ * 架构/特性; "MiniMax-M3の効率的な推論サービス" on news.chathome.org; the MSA
+ * paragraph of "NVIDIA 加速インフラ上で MiniMax M3 を活用した長文脈推論..." on
+ * news.ainew.jp) has two halves: a score part that picks, per KV group, the
+ * most relevant 128-token KV blocks, and dense attention of the query heads
+ * over only those blocks.  The six compute calls below are the steps of that
+ * path: index scoring, top-k block selection, page-table build, sparse decode
+ * attention, KV-block-major sparse prefill attention and the log-sum-exp merge.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every call returns an msa_status_t.  On an error nothing is launched and
+ *    msa_last_error() holds a thread-local description.
+ *  - Calls are asynchronous on the caller's HIP stream (NULL = the default
+ *    stream).  They never synchronise and never allocate device memory.
+ *  - The caller owns every buffer.  Array arguments are device pointers on the
+ *    current device unless stated otherwise; the library keeps no pointer after
+ *    a call returns.
+ *  - Host-side validation covers scalars, pointers, alignment and strides.  The
+ *    values inside device index arrays (row_pos, row_req, block_table, sel,
+ *    page_table, blk_lo) cannot be checked from the host: keeping them in range
+ *    is a precondition, and a violation is undefined behaviour (typically a
+ *    memory fault reported by the caller's next synchronisation).
+ *  - Outputs are written in full, padding included (-inf scores, -1 indices,
+ *    zero partial outputs with -inf log-sum-exp).
+ *  - bf16 is stored as its 16-bit pattern (the top half of an IEEE float).
+ *  - Blocks and cache pages are 128 tokens (dims.blk must be 128).  Block b of
+ *    a request covers positions [128 b, 128 b + 127]; a row at position pos
+ *    owns block own = pos / 128 and sees positions <= pos only (causal).
+ *  - The library is stateless and thread-safe.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSA_OK = 0,
+    MSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    MSA_ERR_INVALID = 2,     /* a size, stride or alignment is invalid */
+    MSA_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. D != 128) */
+    MSA_ERR_WORKSPACE = 4,   /* workspace too small */
+    MSA_ERR_HIP = 5          /* a HIP launch failed */
+} msa_status_t;
+
+/* A HIP stream (hipStream_t); NULL selects the default stream. */
+typedef void *msa_stream_t;
+
+/* Model dimensions.
+ *   G      KV groups (KV heads)                       >= 1
+ *   Hg     query heads per KV group; head h uses group h / Hg; Hg in {1,2,4,8,16}
+ *   D      head dimension                             == 128
+ *   n_idx  query-side index vectors per (row, group)  1 .. 16
+ *   d_idx  index-vector dimension                     64 or 128
+ *   blk    tokens per block and per cache page        == 128 */
+typedef struct {
+    int32_t G, Hg, D, n_idx, d_idx, blk;
+} msa_dims_t;
+
+/* A paged cache tensor: element (page, group, token, dim) of a bf16 cache lives
+ * at base + page*page_stride + group*group_stride + token*token_stride + dim
+ * (strides in elements; the dim stride is 1).  base must be 16-byte aligned
+ * and every stride a multiple of 8.  The default layout [page][G][128][dim]
+ * is page_stride = G*128*dim, group_stride = 128*dim, token_stride = dim; a
+ * token-major cache [page][128][G][dim] is group_stride = dim,
+ * token_stride = G*dim. */
+typedef struct {
+    const void *base;
+    int64_t page_stride, group_stride, token_stride;
+} msa_view_t;
+
+/* ------------------------------------------------------------------ a1 / a6
+ * msa_index_score -- block scores from the index vectors.
+ * Pages: decode index-scoring section (解码索引评分内核优化) of the aihot.news
+ * page: query-side index vectors are compared with every candidate key-side
+ * index vector, each 128-token block reduces to a single score, and every
+ * request and K group has its own candidate block range and mask.
+ *
+ * For row r (request req = row_req[r], position pos = row_pos[r], own = pos/128),
+ * group g and block b in [0, score_stride):
+ *     scored iff b == own or lo <= b < own   (lo = blk_lo[req][g], or 0)
+ *     scores[r][g][b] = max over tokens t of block b with 128 b + t <= pos of
+ *                       sum_{j < n_idx} dot(q_idx[r][g][j], k_idx[page][g][t]) / sqrt(d_idx)
+ *     where page = block_table[req][b]; unscored blocks get -inf.
+ * (The block reduction -- max over tokens of the summed index dot products --
+ * is this library's reading; the pages leave it open.)
+ *
+ *   q_idx        bf16 [rows][G][n_idx][d_idx], contiguous, 16-byte aligned
+ *   k_idx        key-index cache view, dim = d_idx
+ *   block_table  int32 [num_reqs][bt_stride]: logical block -> physical page
+ *   row_req      int32 [rows], or NULL when row r is request r
+ *   row_pos      int32 [rows]
+ *   blk_lo       int32 [num_reqs][G], or NULL for lo = 0
+ *   num_reqs     number of requests (rows of block_table); a hint for the
+ *                schedule (many rows per request -> tiled matrix-core path)
+ *   scores       fp32 [rows][G][score_stride]; score_stride > own of every row
+ * Accumulation is fp32 from bf16 inputs. */
+msa_status_t msa_index_score(const msa_dims_t *dims, int32_t rows, const void *q_idx,
+                             msa_view_t k_idx, const int32_t *block_table, int32_t bt_stride,
+                             const int32_t *row_req, const int32_t *row_pos,
+                             const int32_t *blk_lo, int32_t num_reqs, float *scores,
+                             int32_t score_stride, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ a2 / a7
+ * msa_topk_blocks -- per (row, group) block selection.
+ * Pages: the score part picks the K most relevant blocks for each KV group
+ * (架构/特性); each request and group has its own top-k boundary
+ * (解码索引评分内核优化).
+ *
+ * Candidates are the blocks b < own with a score other than -inf.  They are
+ * ranked by score descending, ties going to the lower block index; the first
+ * min(k, #candidates) are kept, the own block is added, and the selection is
+ * written in ascending block order to sel[r][g][0 .. k], padded with -1.
+ *
+ *   scores   fp32 [rows][G][score_stride] (as written by msa_index_score)
+ *   row_pos  int32 [rows]
+ *   k        0 <= k; nslot = k + 1 entries per (row, group)
+ *   sel      int32 [rows][G][k + 1] */
+msa_status_t msa_topk_blocks(const msa_dims_t *dims, int32_t rows, const float *scores,
+                             int32_t score_stride, const int32_t *row_pos, int32_t k,
+                             int32_t *sel, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ a3
+ * msa_build_page_table -- physical page of every selected block.
+ * Pages: paged-attention integration section (将 MSA 与分页注意力集成): build a
+ * page table from the selected blocks with the KV-group dimension folded into
+ * the batch, so every (row, group) has a page list of its own.
+ *
+ *   page_table[r][g][s] = block_table[row_req[r]][sel[r][g][s]], -1 stays -1.
+ *   sel, page_table  int32 [rows][G][nslot]
+ *   row_req          int32 [rows] or NULL (row r is request r)
+ *   block_table      int32 [num_reqs][bt_stride] */
+msa_status_t msa_build_page_table(const msa_dims_t *dims, int32_t rows, const int32_t *sel,
+                                  int32_t nslot, const int32_t *row_req,
+                                  const int32_t *block_table, int32_t bt_stride,
+                                  int32_t *page_table, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ a4
+ * msa_sparse_attn_decode -- per-block partial attention for decode rows.
+ * Pages: dense attention over the selected blocks (架构/特性), read through the
+ * per-group page table (将 MSA 与分页注意力集成).
+ *
+ * For row r, head h (group g = h / Hg) and slot s with sel[r][g][s] = b >= 0:
+ * softmax attention of q[r][h] over the tokens t of page page_table[r][g][s]
+ * with 128 b + t <= row_pos[r], logits scaled by sm_scale:
+ *     o_part[r][h][s][:] = normalised output (bf16),
+ *     lse_part[r][h][s]  = m + ln(sum exp(z - m)) in natural log (fp32).
+ * Empty slots get o = 0 and lse = -inf.  Combine with msa_lse_merge.
+ *
+ *   q         bf16 [rows][G*Hg][D], contiguous, 16-byte aligned
+ *   k, v      key / value cache views, dim = D
+ *   sel, page_table  int32 [rows][G][nslot]
+ *   o_part    bf16 [rows][G*Hg][nslot][D];  lse_part fp32 [rows][G*Hg][nslot]
+ * bf16 inputs, fp32 accumulation on the matrix cores. */
+msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const void *q,
+                                    msa_view_t k, msa_view_t v, const int32_t *sel,
+                                    const int32_t *page_table, int32_t nslot,
+                                    const int32_t *row_pos, float sm_scale, void *o_part,
+                                    float *lse_part, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ a8 / a9
+ * msa_sparse_attn_prefill -- KV-block-major sparse attention.
+ * Pages: KV-block-major section (KV 块主序稀疏注意力): many queries select the
+ * same KV block, so the {query, block} map is inverted into {block, queries}
+ * and the block loop runs outside the query loop; every KV block is moved from
+ * HBM once and yields partial outputs that a log-sum-exp reduction combines.
+ *
+ * Same inputs and outputs as msa_sparse_attn_decode (the results are identical
+ * to it row by row).  Internally it inverts sel into per-(group, page) query
+ * lists in the workspace, then runs one pass per KV page that loads K and V
+ * once and serves every (row, slot) that selected it.
+ *
+ *   num_pages   number of pages in the caches (page_table values < num_pages)
+ *   workspace   device buffer of at least msa_prefill_workspace_size() bytes,
+ *               16-byte aligned; contents on entry are ignored */
+msa_status_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t rows, int32_t nslot,
+                                        int32_t num_pages, size_t *bytes);
+
+msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t rows, const void *q,
+                                     msa_view_t k, msa_view_t v, const int32_t *sel,
+                                     const int32_t *page_table, int32_t nslot,
+                                     const int32_t *row_pos, int32_t num_pages, float sm_scale,
+                                     void *workspace, size_t workspace_bytes, void *o_part,
+                                     float *lse_part, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ a5 / a10
+ * msa_lse_merge -- log-sum-exp reduction of per-block partials.
+ * Pages: the final reduction rescales the partial O outputs by their
+ * log-sum-exp and sums them (KV 块主序稀疏注意力; the page's own formula did not
+ * survive, this is the standard one):
+ *     m = max_s lse_s,  w_s = exp(lse_s - m),
+ *     o = sum_s w_s o_s / sum_s w_s,  lse = m + ln(sum_s w_s)
+ * Slots with lse = -inf are skipped; a (row, head) with none gets o = 0 and
+ * lse = -inf.
+ *
+ *   o_part  bf16 [rows][H][nslot][D];  lse_part fp32 [rows][H][nslot]
+ *   o       bf16 [rows][H][D];         lse      fp32 [rows][H] (may be NULL)
+ *   D must be 128. */
+msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D,
+                           const void *o_part, const float *lse_part, void *o, float *lse,
+                           msa_stream_t stream);
+
+/* ------------------------------------------------------------------ misc */
+const char *msa_version(void);
+const char *msa_status_string(msa_status_t s);
+/* Thread-local description of the last error on this thread ("" if none). */
+const char *msa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

@@ -1,0 +1,100 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times.  The oracle recomputes sampled rows one by one (every group and
+block of each sampled row); the whole selection and every partial of the
+block-major prefill are also checked against properties that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import msa_synth
+import oracle
+import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_ROWS = {
+    1: [0],
+    2: [0, 5],
+    3: None,            # shortest and longest request, chosen below
+    4: [0, 1, 127, 128, 4095, 8191],
+    5: [2],
+}
+
+
+def _rows(cfg, case):
+    if SAMPLE_ROWS[cfg] is not None:
+        return SAMPLE_ROWS[cfg]
+    L = case.ctx_len.cpu().numpy()
+    return [int(np.argmin(L)), int(np.argmax(L))]
+
+
+def _check_whole_selection(case, res):
+    """Properties of every (row, group) at full size: ascending, own last, -1
+    padded, count = min(k, #candidates) + 1, all selected blocks scored."""
+    sel = res["sel"].numpy()
+    scores = res["scores"].numpy()
+    pos = case.row_pos.cpu().numpy()
+    own = pos // 128
+    valid = sel >= 0
+    n = valid.sum(-1)
+    ncand = np.array([[np.isfinite(scores[r, g, :own[r]]).sum() for g in range(case.G)]
+                      for r in range(case.rows)]) if case.rows <= 64 else None
+    last = np.take_along_axis(sel, (n - 1)[..., None], -1)[..., 0]
+    assert np.all(last == own[:, None]), "own block must be the last valid entry"
+    both = valid[..., 1:] & valid[..., :-1]
+    assert np.all((np.diff(sel, axis=-1) > 0) | ~both), "selection must be strictly ascending"
+    assert np.all(valid[..., :1]) and np.all(np.diff(valid.astype(int), axis=-1) <= 0)
+    if ncand is not None:
+        assert np.array_equal(n, np.minimum(case.k, ncand) + 1)
+    picked = np.take_along_axis(scores, np.maximum(sel, 0), -1)
+    assert np.all(np.isfinite(picked[valid])), "a selected block was not scored"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_full_size(cfg):
+    print(f"[case] config {cfg} full size", flush=True)
+    case = msa_synth.config_case(cfg, device="cuda")
+    res = pu.gpu_path(case)
+    _check_whole_selection(case, res)
+    rows = _rows(cfg, case)
+    s_ref = pu.oracle_scores(case, rows)
+    pu.check_scores(res["scores"].numpy()[rows], s_ref)
+    pos = case.row_pos.cpu().numpy()[rows]
+    sel_ref = oracle.topk(s_ref.astype(np.float32), pos, case.k)
+    ntie = pu.check_selection(res["sel"].numpy()[rows], sel_ref, s_ref, pos, case.k)
+    print(f"  rows {rows}: near-tie exemptions {ntie}", flush=True)
+    pt_ref = oracle.page_table(res["sel"].numpy()[rows], case.block_table.cpu().numpy(),
+                               case.row_req.cpu().numpy()[rows])
+    assert np.array_equal(res["pt"].numpy()[rows], pt_ref)
+    op, lp, o, lse = pu.oracle_attn(case, rows, res["sel"].numpy()[rows], res["pt"].numpy()[rows])
+    pu.check_partials(res["o_part"][rows], res["lse_part"][rows], op, lp)
+    pu.check_output(res["o"][rows], res["lse"][rows], o, lse)
+    if cfg == 4:
+        # every partial of the block-major kernel equals the per-row kernel's, bit for bit
+        dec = pu.gpu_path(case, prefill=False, sel=res["sel"].cuda(), pt=res["pt"].cuda())
+        assert torch.equal(dec["o_part"], res["o_part"])
+        assert torch.equal(dec["lse_part"], res["lse_part"])
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_config3_lower_bounds():
+    """Ragged batch with per-(request, group) lower candidate bounds."""
+    print("[case] config 3 with lower bounds", flush=True)
+    case = msa_synth.config_case(3, device="cuda", lo_frac=0.25)
+    res = pu.gpu_path(case)
+    rows = [0, 17]
+    s_ref = pu.oracle_scores(case, rows)
+    pu.check_scores(res["scores"].numpy()[rows], s_ref)
+    pos = case.row_pos.cpu().numpy()[rows]
+    sel_ref = oracle.topk(s_ref.astype(np.float32), pos, case.k)
+    pu.check_selection(res["sel"].numpy()[rows], sel_ref, s_ref, pos, case.k)
+    lo = case.blk_lo.cpu().numpy()
+    sel = res["sel"].numpy()
+    own = case.row_pos.cpu().numpy() // 128
+    for r in range(case.rows):
+        for g in range(case.G):
+            s = sel[r, g][sel[r, g] >= 0]
+            assert np.all((s >= min(lo[r, g], own[r])) | (s == own[r]))
+    del case
+    torch.cuda.empty_cache()
