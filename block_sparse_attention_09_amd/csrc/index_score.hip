@@ -27,13 +27,26 @@ namespace msa {
 
 namespace {
 
-constexpr int kTilesPerStep = 4;             // 4 x 16 tokens = half a block per step
-constexpr int kStepsPerBlock = kBlk / (16 * kTilesPerStep);
+#ifndef MSA_SCORE_NT
+#define MSA_SCORE_NT 1
+#endif
+
+constexpr int kTilesPerStep = 4;   // 4 x 16 tokens = half a block per register buffer
+constexpr int kMaxChunk = 64;      // chunk length bound: one page id per lane
 
 template <int DIDX>
 struct StepBuf {
     bf16x8 a[kTilesPerStep][DIDX / 32];
 };
+
+// Key-index stream: read once, never reused -> non-temporal loads.
+__device__ __forceinline__ u32x4 ld16_stream(const bf16_t *p) {
+#if MSA_SCORE_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#else
+    return ld16(p);
+#endif
+}
 
 template <int DIDX>
 __device__ __forceinline__ void load_step(StepBuf<DIDX> &buf, const bf16_t *page_base, int64_t kts,
@@ -44,8 +57,29 @@ __device__ __forceinline__ void load_step(StepBuf<DIDX> &buf, const bf16_t *page
         const int tok = (half * kTilesPerStep + ti) * 16 + (lane & 15);
         const bf16_t *p = page_base + (int64_t)tok * kts + kq;
 #pragma unroll
-        for (int c = 0; c < DIDX / 32; ++c) buf.a[ti][c] = as_bf16x8(ld16(p + 32 * c));
+        for (int c = 0; c < DIDX / 32; ++c) buf.a[ti][c] = as_bf16x8(ld16_stream(p + 32 * c));
     }
+}
+
+// Max over the 64 tokens of one half block of qbar . k_t (fp32), tokens after
+// pos masked.  tok_base is the position of this lane's first accumulator row.
+template <int DIDX>
+__device__ __forceinline__ float block_half_max(const StepBuf<DIDX> &buf, const bf16x8 *bhi,
+                                                const bf16x8 *blo, int tok_base, int pos) {
+    float best = -INFINITY;
+#pragma unroll
+    for (int ti = 0; ti < kTilesPerStep; ++ti) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < DIDX / 32; ++c) {
+            d = mfma16(buf.a[ti][c], bhi[c], d);
+            d = mfma16(buf.a[ti][c], blo[c], d);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            best = fmaxf(best, (tok_base + ti * 16 + i <= pos) ? d[i] : -INFINITY);
+    }
+    return best;
 }
 
 template <int DIDX>
@@ -78,28 +112,46 @@ __global__ __launch_bounds__(256) void index_score_stream_kernel(
         if (b < s0 || b >= s1) out[b] = -INFINITY;
     if (s0 >= s1) return;
 
-    // qbar = sum_j q_j in fp32, split into bf16 hi/lo, placed in B column 0.
+    // One round trip for everything the chunk needs besides the stream itself:
+    // the page of every scored block (one per lane) and the query index vectors.
+    const int32_t *bt = block_table + (int64_t)req * bt_stride;
+    const int my_page = (lane < s1 - s0) ? bt[s0 + lane] : 0;
     const int kq = (lane >> 4) * 8;
     const bool col0 = (lane & 15) == 0;
+    const bf16_t *qb = q_idx + ((int64_t)r * G + g) * n_idx * DIDX + kq;
+    float acc[DIDX / 32][8];
+#pragma unroll
+    for (int c = 0; c < DIDX / 32; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+    for (int j0 = 0; j0 < n_idx; j0 += 4) {
+        u32x4 w[4][DIDX / 32];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int c = 0; c < DIDX / 32; ++c)
+                w[jj][c] = (j0 + jj < n_idx) ? ld16(qb + (j0 + jj) * DIDX + 32 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int c = 0; c < DIDX / 32; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[c][2 * e] += bf16_lo(w[jj][c][e]);
+                    acc[c][2 * e + 1] += bf16_hi(w[jj][c][e]);
+                }
+    }
+    // qbar in fp32 -> bf16 hi + lo, placed in B column 0 (lanes 0, 16, 32, 48).
     bf16x8 bhi[DIDX / 32], blo[DIDX / 32];
-    const bf16_t *qb = q_idx + ((int64_t)r * G + g) * n_idx * DIDX;
 #pragma unroll
     for (int c = 0; c < DIDX / 32; ++c) {
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < n_idx; ++j) {
-            const u32x4 w = ld16(qb + j * DIDX + 32 * c + kq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += bf16_lo(w[e]);
-                acc[2 * e + 1] += bf16_hi(w[e]);
-            }
-        }
         u32x4 hw, lw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            uint32_t h0 = f32_to_bf16_rne(acc[2 * e]), h1 = f32_to_bf16_rne(acc[2 * e + 1]);
-            uint32_t l0 = f32_to_bf16_rne(acc[2 * e] - __uint_as_float(h0 << 16));
-            uint32_t l1 = f32_to_bf16_rne(acc[2 * e + 1] - __uint_as_float(h1 << 16));
+            const uint32_t h0 = f32_to_bf16_rne(acc[c][2 * e]);
+            const uint32_t h1 = f32_to_bf16_rne(acc[c][2 * e + 1]);
+            const uint32_t l0 = f32_to_bf16_rne(acc[c][2 * e] - __uint_as_float(h0 << 16));
+            const uint32_t l1 = f32_to_bf16_rne(acc[c][2 * e + 1] - __uint_as_float(h1 << 16));
             hw[e] = col0 ? (h0 | (h1 << 16)) : 0u;
             lw[e] = col0 ? (l0 | (l1 << 16)) : 0u;
         }
@@ -108,45 +160,26 @@ __global__ __launch_bounds__(256) void index_score_stream_kernel(
     }
 
     const int64_t gofs = (int64_t)g * kgs;
-    const int32_t *bt = block_table + (int64_t)req * bt_stride;
-    const int nsteps = (s1 - s0) * kStepsPerBlock;
-
-    StepBuf<DIDX> buf[2];
-    float best = -INFINITY;
-    const bf16_t *page_cur = kbase + (int64_t)bt[s0] * kps + gofs;
-    load_step<DIDX>(buf[0], page_cur, kts, 0, lane);
-
-    for (int step = 0; step < nsteps; ++step) {
-        const int cur = step & 1;
-        const int b = s0 + step / kStepsPerBlock;
-        const int half = step % kStepsPerBlock;
-        // issue the next step's loads (next half, or the next block's page) first
-        if (step + 1 < nsteps) {
-            const int nb_ = s0 + (step + 1) / kStepsPerBlock;
-            const bf16_t *page_next =
-                (nb_ == b) ? page_cur : kbase + (int64_t)bt[nb_] * kps + gofs;
-            load_step<DIDX>(buf[cur ^ 1], page_next, kts, (step + 1) % kStepsPerBlock, lane);
-            if (nb_ != b) page_cur = page_next;
+    const int nblk = s1 - s0;
+    // Two register buffers, one per half block (static indices: no scratch).  The
+    // loads of the next half (or of the next block's page) are issued before the
+    // matrix-core work on the current half.
+    StepBuf<DIDX> bufA, bufB;
+    const bf16_t *page = kbase + (int64_t)__builtin_amdgcn_readlane(my_page, 0) * kps + gofs;
+    load_step<DIDX>(bufA, page, kts, 0, lane);
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int tok_base = (s0 + bi) * kBlk + (lane >> 4) * 4;
+        load_step<DIDX>(bufB, page, kts, 1, lane);
+        float best = block_half_max<DIDX>(bufA, bhi, blo, tok_base, pos);
+        if (bi + 1 < nblk) {
+            page = kbase + (int64_t)__builtin_amdgcn_readlane(my_page, bi + 1) * kps + gofs;
+            load_step<DIDX>(bufA, page, kts, 0, lane);
         }
-#pragma unroll
-        for (int ti = 0; ti < kTilesPerStep; ++ti) {
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < DIDX / 32; ++c) {
-                d = mfma16(buf[cur].a[ti][c], bhi[c], d);
-                d = mfma16(buf[cur].a[ti][c], blo[c], d);
-            }
-            const int tok0 = b * kBlk + (half * kTilesPerStep + ti) * 16 + (lane >> 4) * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) best = fmaxf(best, (tok0 + i <= pos) ? d[i] : -INFINITY);
-        }
-        if (half == kStepsPerBlock - 1) {
-            // column 0 lives in lanes 0, 16, 32, 48
-            float m = wave_max_xor(best, 16);
-            m = wave_max_xor(m, 32);
-            if (lane == 0) out[b] = m * scale;
-            best = -INFINITY;
-        }
+        best = fmaxf(best, block_half_max<DIDX>(bufB, bhi, blo, tok_base + 64, pos));
+        // column 0 of the accumulators lives in lanes 0, 16, 32, 48
+        best = wave_max_xor(best, 16);
+        best = wave_max_xor(best, 32);
+        if (lane == 0) out[s0 + bi] = best * scale;
     }
 }
 
@@ -160,8 +193,12 @@ hipError_t launch_index_score(const msa_dims_t &d, int rows, const bf16_t *q_idx
     (void)num_reqs;
     // Chunk length: enough waves to fill 256 CUs several times over.
     const int64_t pairs = (int64_t)rows * d.G;
-    int cb = (int)((pairs * score_stride) / 16384);
+#ifndef MSA_SCORE_WAVES_TARGET
+#define MSA_SCORE_WAVES_TARGET 4096
+#endif
+    int cb = (int)((pairs * score_stride) / MSA_SCORE_WAVES_TARGET);
     cb = cb < 2 ? 2 : (cb > 16 ? 16 : cb);
+    static_assert(16 <= kMaxChunk, "chunk pages are held one per lane");
     const int nchunk = (score_stride + cb - 1) / cb;
     const int64_t waves = pairs * nchunk;
     const int64_t blocks = (waves + 3) / 4;
