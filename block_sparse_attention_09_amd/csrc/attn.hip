@@ -13,14 +13,17 @@
 //    reduction rescales and sums.
 //
 // One workgroup serves one (KV group, page) unit: it stages K (row-major) and V
-// (transposed) in LDS once, then its four waves take tiles of 16 query rows
-// (16 / Hg query tokens x Hg heads) against the whole 128-token block:
-//   S^T = K Q^T    16x16x32 bf16 MFMA, K from LDS, Q straight from global
+// (transposed) in LDS once, then its four waves take tiles of 32 query rows
+// (32 / Hg query tokens x Hg heads) against the whole 128-token block on the
+// 32x32x16 bf16 matrix cores:
+//   S^T = K Q^T    K from LDS (A), Q straight from global (B)
 //   softmax        per query row over the block's causally visible tokens,
-//                  exp2 with log2(e) folded into the scale
-//   O^T = V^T P^T  16x16x32 bf16 MFMA, P^T repacked in registers to bf16, V^T
-//                  from LDS in the permuted token order that matches it
+//                  exp2 with log2(e) folded into the scale, fp32 row sums
+//   O^T = V^T P^T  V^T from LDS in the token order that matches where the S^T
+//                  accumulators leave P, P^T repacked to bf16 in registers
 // and writes the normalised partial (bf16) and its natural-log LSE (fp32).
+// A wave needs about 200 registers, so two workgroups (eight waves) share a CU
+// and one wave's softmax overlaps another's matrix-core work.
 // Decode units hold one query row each; prefill units come from a counting-sort
 // inversion of the selection built in the caller's workspace.
 #include "msa_internal.h"
@@ -40,11 +43,11 @@ struct AttnSmem {
     bf16_t vt[128 * KST];   // V page, [dim][permuted token position]
 };
 
-// LDS column of token t in V^T.  Within each 32-token chunk the MFMA K index
-// k = 8 b + 4 a + c holds token 16 a + 4 b + c, which is where the S^T
-// accumulators of tiles (2 kc, 2 kc + 1) leave P in each lane.
+// LDS column of token t in V^T.  In every 16-token PV step the MFMA K index
+// k = 8 h + 4 q + r holds token 8 q + 4 h + r of the step, which is where the
+// S^T accumulators leave P in lane half h: swap bits 2 and 3 of t.
 __device__ __forceinline__ int vt_col(int t) {
-    return (t & ~31) | (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
+    return (t & ~15) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2) | (t & 3);
 }
 
 __device__ __forceinline__ bf16x8 lds16(const bf16_t *p) {
@@ -78,98 +81,6 @@ __device__ __forceinline__ void stage_kv(AttnSmem &sm, const bf16_t *kp, int64_t
     }
 }
 
-// Attention of query tiles tile_begin, tile_begin + tile_step, ... of a unit's
-// query list against the block staged in LDS.  Entry e of the list is
-// row * nslot + slot.  Every lane owns query row (lane & 15) of the tile.
-template <int HG, typename QList>
-__device__ __forceinline__ void attend_tiles(const AttnSmem &sm, const AttnArgs &a, int g,
-                                             QList qlist, int nq, int tile_begin, int tile_step,
-                                             float scale_log2) {
-    constexpr int QPT = 16 / HG;  // query tokens per 16-row tile
-    const int lane = threadIdx.x & 63;
-    const int c = lane & 15, grp = lane >> 4;
-    const int H = a.G * HG;
-    const int ntiles = (nq + QPT - 1) / QPT;
-    for (int tile = tile_begin; tile < ntiles; tile += tile_step) {
-        const int qi = tile * QPT + c / HG;
-        const bool valid = qi < nq;
-        const int entry = qlist(valid ? qi : tile * QPT);
-        const int row = entry / a.nslot, slot = entry - row * a.nslot;
-        const int h = g * HG + (c % HG);
-        const int blk = a.sel[((int64_t)row * a.G + g) * a.nslot + slot];
-        const int vis = valid ? (a.row_pos[row] - blk * kBlk) : -1;  // tokens t <= vis
-
-        const bf16_t *qp = a.q + ((int64_t)row * H + h) * 128 + 8 * grp;
-        bf16x8 qb[4];
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) qb[c4] = as_bf16x8(ld16(qp + 32 * c4));
-
-        f32x4 s[8];
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4)
-                s[mt] = mfma16(lds16(&sm.k[(16 * mt + c) * KST + 32 * c4 + 8 * grp]), qb[c4], s[mt]);
-        }
-
-        float m = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * mt + 4 * grp + i;
-                const float z = (t <= vis) ? s[mt][i] * scale_log2 : -INFINITY;
-                s[mt][i] = z;
-                m = fmaxf(m, z);
-            }
-        m = wave_max_xor(m, 16);
-        m = wave_max_xor(m, 32);
-        const float msafe = (m == -INFINITY) ? 0.f : m;
-        float l = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(s[mt][i] - msafe);
-                s[mt][i] = p;
-                l += p;
-            }
-        l = wave_sum_xor(l, 16);
-        l = wave_sum_xor(l, 32);
-
-        f32x4 o[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            u32x4 pw;
-            pw[0] = pack_bf16x2(s[2 * kc][0], s[2 * kc][1]);
-            pw[1] = pack_bf16x2(s[2 * kc][2], s[2 * kc][3]);
-            pw[2] = pack_bf16x2(s[2 * kc + 1][0], s[2 * kc + 1][1]);
-            pw[3] = pack_bf16x2(s[2 * kc + 1][2], s[2 * kc + 1][3]);
-            const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                o[dt] = mfma16(lds16(&sm.vt[(16 * dt + c) * KST + 32 * kc + 8 * grp]), pb, o[dt]);
-        }
-
-        if (valid) {
-            const float inv = 1.f / l;
-            const int64_t oi = ((int64_t)row * H + h) * a.nslot + slot;
-            bf16_t *op = a.o_part + oi * 128 + 4 * grp;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                uint2 w;
-                w.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-                w.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-                *reinterpret_cast<uint2 *>(op + 16 * dt) = w;
-            }
-            if (grp == 0) a.lse_part[oi] = (m + __builtin_amdgcn_logf(l)) * kLn2;
-        }
-    }
-}
-
 // o = 0, lse = -inf for the Hg heads of an empty (row, group, slot).
 template <int HG>
 __device__ __forceinline__ void write_empty_slot(const AttnArgs &a, int r, int g, int s, int tid,
@@ -183,47 +94,197 @@ __device__ __forceinline__ void write_empty_slot(const AttnArgs &a, int r, int g
     }
 }
 
-struct SingleEntry {
-    int e;
-    __device__ int operator()(int) const { return e; }
+// Forces the compiler to have x in registers at this point.  Loads and stores
+// share one completion counter on this architecture, so once a store is
+// outstanding, waiting for any load waits for the store too; the wave therefore
+// takes delivery of everything it prefetched just before it issues its stores.
+template <typename T>
+__device__ __forceinline__ void take_delivery(const T &x) {
+    asm volatile("" ::"v"(x));
+}
+
+// Per-lane metadata of one query tile (this lane's query row), kept raw so
+// that its loads stay in flight until the tile is processed.
+struct TileMeta {
+    int row, slot, pos, blk;
+    bool valid;
 };
 
-struct ListEntry {
-    const int32_t *p;
-    __device__ int operator()(int i) const { return p[i]; }
-};
-
-// ------------------------------------------------------------------ decode
+// One wave's share of a unit: tiles w, w + 4, ... of 32 query rows each.
+// Lane l owns query row l % 32 of the tile; lane half h = l / 32 picks which
+// tokens (S^T rows) and head dimensions (O^T rows) it holds.
 template <int HG>
-__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a, float scale_log2) {
-    __shared__ AttnSmem sm;
-    const int unit = blockIdx.x;  // (r, g, s)
-    const int s = unit % a.nslot;
-    const int rg = unit / a.nslot;
-    const int g = rg % a.G, r = rg / a.G;
-    const int blk = a.sel[unit];
-    if (blk < 0) {
-        write_empty_slot<HG>(a, r, g, s, threadIdx.x, kAttnThreads);
-        return;
+__device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, const AttnArgs &a, int g,
+                                                const int32_t *__restrict__ lst, int nq,
+                                                float scale_log2) {
+    constexpr int QPT = 32 / HG;  // query tokens per tile
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = lane & 31, h = lane >> 5;
+    const int H = a.G * HG;
+    const int ntiles = (nq + QPT - 1) / QPT;
+    const int my_tiles = ntiles > w ? (ntiles - w + kAttnWaves - 1) / kAttnWaves : 0;
+    if (my_tiles == 0) return;
+    const int hh = j % HG;
+
+    auto qidx = [&](int t) { return (w + kAttnWaves * t) * QPT + j / HG; };
+    auto entry_of = [&](int t) {
+        const int qi = qidx(t);
+        return lst[(t < my_tiles && qi < nq) ? qi : 0];
+    };
+    auto load_q = [&](bf16x8 (&qb)[8], int entry) {
+        const int row = entry / a.nslot;
+        const bf16_t *qp = a.q + ((int64_t)row * H + g * HG + hh) * 128 + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qb[ks] = as_bf16x8(ld16(qp + 16 * ks));
+    };
+    auto load_meta = [&](int entry, int t) {
+        TileMeta m;
+        m.row = entry / a.nslot;
+        m.slot = entry - m.row * a.nslot;
+        m.pos = a.row_pos[m.row];
+        m.blk = a.sel[((int64_t)m.row * a.G + g) * a.nslot + m.slot];
+        m.valid = t < my_tiles && qidx(t) < nq;
+        return m;
+    };
+
+    bf16x8 qb[8];
+    const int e0 = entry_of(0);
+    load_q(qb, e0);
+    TileMeta meta = load_meta(e0, 0);
+    int ent_next = entry_of(1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) take_delivery(qb[ks]);
+    take_delivery(meta.pos);
+    take_delivery(meta.blk);
+    take_delivery(ent_next);
+
+    for (int t = 0; t < my_tiles; ++t) {
+        // K and V^T operands are re-read from LDS for every tile: without this
+        // barrier the compiler hoists all 64 fragment reads out of the loop
+        // into registers and the wave no longer fits two per SIMD
+        asm volatile("" ::: "memory");
+        // S^T = K Q^T: four 32-token row tiles, 8 dimension steps of 16
+        f32x16 s[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) s[mt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                s[mt] = mfma32(lds16(&sm.k[(32 * mt + j) * KST + 16 * ks + 8 * h]), qb[ks], s[mt]);
+
+        // the next tile's query rows (into the registers just consumed) and metadata
+        const bool more = t + 1 < my_tiles;
+        TileMeta meta_next = meta;
+        if (more) {
+            load_q(qb, ent_next);
+            meta_next = load_meta(ent_next, t + 1);
+            ent_next = entry_of(t + 2);
+        }
+
+        // softmax over the block: element 4 q + r of s[mt] is token 32 mt + 8 q + 4 h + r
+        const int vis = meta.valid ? meta.pos - meta.blk * kBlk : -1;
+        float mx = -INFINITY;
+        if (__builtin_amdgcn_readfirstlane(__all(vis >= kBlk - 1))) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int tok = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+                    s[mt][e] = (tok <= vis) ? s[mt][e] : -INFINITY;
+                    mx = fmaxf(mx, s[mt][e]);
+                }
+        }
+        mx = wave_max_xor(mx, 32);
+        const float off = (mx == -INFINITY) ? 0.f : -mx * scale_log2;
+        float l = 0.f;
+        bf16x8 pb[8];  // P^T operand of PV step ks: elements 8 (ks % 2) .. +8 of s[ks / 2]
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + e], scale_log2, off));
+                l += p[e];
+            }
+            u32x4 pw;
+            pw[0] = pack_bf16x2(p[0], p[1]);
+            pw[1] = pack_bf16x2(p[2], p[3]);
+            pw[2] = pack_bf16x2(p[4], p[5]);
+            pw[3] = pack_bf16x2(p[6], p[7]);
+            pb[ks] = as_bf16x8(pw);
+        }
+        l = wave_sum_xor(l, 32);
+
+        // O^T = V^T P^T: four 32-dim row tiles, 8 token steps of 16
+        f32x16 o[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                o[dt] = mfma32(lds16(&sm.vt[(32 * dt + j) * KST + 16 * ks + 8 * h]), pb[ks], o[dt]);
+
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) take_delivery(qb[ks]);
+        take_delivery(meta_next.pos);
+        take_delivery(meta_next.blk);
+        take_delivery(ent_next);
+        // normalised partial: element 4 q + r of o[dt] is dim 32 dt + 8 q + 4 h + r.
+        // One lane-half swap per packed pair gives each lane 8 contiguous dims
+        // twice per 32-dim tile (lower half: 0..7 and 16..23, upper: 8..15 and
+        // 24..31), so every 16-byte store fills 32 contiguous bytes of a row.
+        if (meta.valid) {
+            const float inv = 1.f / l;
+            const int64_t oi = ((int64_t)meta.row * H + g * HG + hh) * a.nslot + meta.slot;
+            bf16_t *op = a.o_part + oi * 128 + 8 * h;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                uint32_t pk[4][2];  // [q][pair]: dims 8 q + 4 h + {0,1}, {2,3}
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pk[q][0] = pack_bf16x2(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv);
+                    pk[q][1] = pack_bf16x2(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
+                }
+                // A = q 0 and 2 (kept by the lower half), B = q 1 and 3 (kept by the upper)
+                u32x4 c0, c1;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const auto x = __builtin_amdgcn_permlane32_swap(pk[0][i], pk[1][i], false, false);
+                    const auto y = __builtin_amdgcn_permlane32_swap(pk[2][i], pk[3][i], false, false);
+                    c0[i] = x[0];
+                    c0[2 + i] = x[1];
+                    c1[i] = y[0];
+                    c1[2 + i] = y[1];
+                }
+                *reinterpret_cast<u32x4 *>(op + 32 * dt) = c0;
+                *reinterpret_cast<u32x4 *>(op + 32 * dt + 16) = c1;
+            }
+            if (h == 0) a.lse_part[oi] = (mx * scale_log2 + __builtin_amdgcn_logf(l)) * kLn2;
+        }
+        meta = meta_next;
     }
-    const int64_t page = a.page_table[unit];
-    stage_kv(sm, a.k + page * a.kps + (int64_t)g * a.kgs, a.kts,
-             a.v + page * a.vps + (int64_t)g * a.vgs, a.vts);
-    __syncthreads();
-    if ((threadIdx.x >> 6) == 0)
-        attend_tiles<HG>(sm, a, g, SingleEntry{r * a.nslot + s}, 1, 0, 1, scale_log2);
 }
 
 // ------------------------------------------------------------------ prefill
 // Workspace: counts[G*P] | offs[G*P + 1] | list[rows*G*nslot] (int32 each).
+// Units are numbered u = page * G + g, so that with the default round-robin
+// dispatch over the 8 XCDs the units of one KV group (and its query rows) stay
+// on one XCD's L2 when G is 8.
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
 }
 
-// Count queries per (group, page); empty slots get their zero partials here.
+// Count queries per (page, group); empty slots get their zero partials here.
 template <int HG>
-__global__ void remap_count_kernel(AttnArgs a, int P, int32_t *__restrict__ counts) {
+__global__ void remap_count_kernel(AttnArgs a, int32_t *__restrict__ counts) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t n = (int64_t)a.rows * a.G * a.nslot;
     if (i >= n) return;
@@ -234,7 +295,7 @@ __global__ void remap_count_kernel(AttnArgs a, int P, int32_t *__restrict__ coun
         write_empty_slot<HG>(a, r, g, s, 0, 1);
         return;
     }
-    atomicAdd(&counts[(int64_t)g * P + a.page_table[i]], 1);
+    atomicAdd(&counts[(int64_t)a.page_table[i] * a.G + g], 1);
 }
 
 // Single-workgroup exclusive scan of counts into offs (n + 1 entries); counts
@@ -249,7 +310,6 @@ __global__ __launch_bounds__(kScanThreads) void remap_scan_kernel(int32_t *__res
     const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
     int local = 0;
     for (int i = b0; i < b1; ++i) local += counts[i];
-    // inclusive scan inside the wave
     int incl = local;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -270,7 +330,7 @@ __global__ __launch_bounds__(kScanThreads) void remap_scan_kernel(int32_t *__res
     if (tid == kScanThreads - 1) offs[n] = before + incl;
 }
 
-__global__ void remap_scatter_kernel(AttnArgs a, int P, int32_t *__restrict__ cursor,
+__global__ void remap_scatter_kernel(AttnArgs a, int32_t *__restrict__ cursor,
                                      const int32_t *__restrict__ offs, int32_t *__restrict__ list) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t n = (int64_t)a.rows * a.G * a.nslot;
@@ -278,25 +338,50 @@ __global__ void remap_scatter_kernel(AttnArgs a, int P, int32_t *__restrict__ cu
     const int s = (int)(i % a.nslot);
     const int rg = (int)(i / a.nslot);
     const int g = rg % a.G, r = rg / a.G;
-    const int64_t u = (int64_t)g * P + a.page_table[i];
+    const int64_t u = (int64_t)a.page_table[i] * a.G + g;
     const int at = atomicAdd(&cursor[u], 1);
     list[offs[u] + at] = r * a.nslot + s;
 }
 
 template <int HG>
-__global__ __launch_bounds__(kAttnThreads) void attn_blockmajor_kernel(
-    AttnArgs a, int P, const int32_t *__restrict__ offs, const int32_t *__restrict__ list,
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_blockmajor_kernel(
+    AttnArgs a, const int32_t *__restrict__ offs, const int32_t *__restrict__ list,
     float scale_log2) {
     __shared__ AttnSmem sm;
-    const int64_t u = blockIdx.x;  // (group, page)
+    const int64_t u = blockIdx.x;  // page * G + group
     const int o0 = offs[u], nq = offs[u + 1] - o0;
     if (nq == 0) return;
-    const int g = (int)(u / P);
-    const int64_t page = u % P;
+    const int g = (int)(u % a.G);
+    const int64_t page = u / a.G;
     stage_kv(sm, a.k + page * a.kps + (int64_t)g * a.kgs, a.kts,
              a.v + page * a.vps + (int64_t)g * a.vgs, a.vts);
     __syncthreads();
-    attend_tiles<HG>(sm, a, g, ListEntry{list + o0}, nq, threadIdx.x >> 6, kAttnWaves, scale_log2);
+    blockmajor_wave<HG>(sm, a, g, list + o0, nq, scale_log2);
+}
+
+// ------------------------------------------------------------------ decode
+// One workgroup per (row, group, slot): the selected page's K/V are staged in
+// LDS and wave 0 serves the row's Hg heads with the same per-wave code as the
+// block-major kernel (so both give bit-identical partials).
+template <int HG>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a, float scale_log2) {
+    __shared__ AttnSmem sm;
+    __shared__ int32_t entry;
+    const int unit = blockIdx.x;  // (r, g, s)
+    const int s = unit % a.nslot;
+    const int rg = unit / a.nslot;
+    const int g = rg % a.G, r = rg / a.G;
+    const int blk = a.sel[unit];
+    if (blk < 0) {
+        write_empty_slot<HG>(a, r, g, s, threadIdx.x, kAttnThreads);
+        return;
+    }
+    const int64_t page = a.page_table[unit];
+    if (threadIdx.x == 0) entry = r * a.nslot + s;
+    stage_kv(sm, a.k + page * a.kps + (int64_t)g * a.kgs, a.kts,
+             a.v + page * a.vps + (int64_t)g * a.vgs, a.vts);
+    __syncthreads();
+    if ((threadIdx.x >> 6) == 0) blockmajor_wave<HG>(sm, a, g, &entry, 1, scale_log2);
 }
 
 }  // namespace
@@ -334,22 +419,22 @@ hipError_t launch_attn_prefill(const AttnArgs &a, int P, void *workspace, hipStr
                        counts, units, 0);
     const dim3 eg((unsigned)((n + 255) / 256)), eb(256);
     switch (a.Hg) {
-        case 1: hipLaunchKernelGGL(remap_count_kernel<1>, eg, eb, 0, stream, a, P, counts); break;
-        case 2: hipLaunchKernelGGL(remap_count_kernel<2>, eg, eb, 0, stream, a, P, counts); break;
-        case 4: hipLaunchKernelGGL(remap_count_kernel<4>, eg, eb, 0, stream, a, P, counts); break;
-        case 8: hipLaunchKernelGGL(remap_count_kernel<8>, eg, eb, 0, stream, a, P, counts); break;
-        default: hipLaunchKernelGGL(remap_count_kernel<16>, eg, eb, 0, stream, a, P, counts); break;
+        case 1: hipLaunchKernelGGL(remap_count_kernel<1>, eg, eb, 0, stream, a, counts); break;
+        case 2: hipLaunchKernelGGL(remap_count_kernel<2>, eg, eb, 0, stream, a, counts); break;
+        case 4: hipLaunchKernelGGL(remap_count_kernel<4>, eg, eb, 0, stream, a, counts); break;
+        case 8: hipLaunchKernelGGL(remap_count_kernel<8>, eg, eb, 0, stream, a, counts); break;
+        default: hipLaunchKernelGGL(remap_count_kernel<16>, eg, eb, 0, stream, a, counts); break;
     }
     hipLaunchKernelGGL(remap_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, offs,
                        (int)units);
-    hipLaunchKernelGGL(remap_scatter_kernel, eg, eb, 0, stream, a, P, counts, offs, list);
+    hipLaunchKernelGGL(remap_scatter_kernel, eg, eb, 0, stream, a, counts, offs, list);
     const dim3 grid((unsigned)units), block(kAttnThreads);
     switch (a.Hg) {
-        case 1: hipLaunchKernelGGL(attn_blockmajor_kernel<1>, grid, block, 0, stream, a, P, offs, list, sl2); break;
-        case 2: hipLaunchKernelGGL(attn_blockmajor_kernel<2>, grid, block, 0, stream, a, P, offs, list, sl2); break;
-        case 4: hipLaunchKernelGGL(attn_blockmajor_kernel<4>, grid, block, 0, stream, a, P, offs, list, sl2); break;
-        case 8: hipLaunchKernelGGL(attn_blockmajor_kernel<8>, grid, block, 0, stream, a, P, offs, list, sl2); break;
-        default: hipLaunchKernelGGL(attn_blockmajor_kernel<16>, grid, block, 0, stream, a, P, offs, list, sl2); break;
+        case 1: hipLaunchKernelGGL(attn_blockmajor_kernel<1>, grid, block, 0, stream, a, offs, list, sl2); break;
+        case 2: hipLaunchKernelGGL(attn_blockmajor_kernel<2>, grid, block, 0, stream, a, offs, list, sl2); break;
+        case 4: hipLaunchKernelGGL(attn_blockmajor_kernel<4>, grid, block, 0, stream, a, offs, list, sl2); break;
+        case 8: hipLaunchKernelGGL(attn_blockmajor_kernel<8>, grid, block, 0, stream, a, offs, list, sl2); break;
+        default: hipLaunchKernelGGL(attn_blockmajor_kernel<16>, grid, block, 0, stream, a, offs, list, sl2); break;
     }
     return hipGetLastError();
 }

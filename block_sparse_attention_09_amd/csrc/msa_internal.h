@@ -15,6 +15,7 @@ constexpr int kWave = 64;   // CDNA wavefront
 typedef uint16_t bf16_t;                                              // bf16 bit pattern
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));            // MFMA A/B operand
 typedef float f32x4 __attribute__((ext_vector_type(4)));              // 16x16 accumulator
+typedef float f32x16 __attribute__((ext_vector_type(16)));            // 32x32 accumulator
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));           // 16-byte load
 
 // ---------------------------------------------------------------- conversions
@@ -27,8 +28,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return u >> 16;
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -39,6 +45,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // D[4 (l / 16) + i][l % 16] for i = 0..3.
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l holds A[l % 32][8 (l / 32) .. +8], B[8 (l / 32) .. +8][l % 32] and
+// D[8 q + 4 (l / 32) + r][l % 32] in element 4 q + r (q, r = 0..3).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

@@ -100,8 +100,9 @@ def build_case(name, *, seed, ctx_lens, G, Hg, d_idx, k, D=128, n_idx=4, paged=T
     """Build one case.
 
     ctx_lens      : tokens in the cache per request (decode rows sit at len-1)
-    prefill_rows  : if > 0, a single request whose last ``prefill_rows`` tokens
-                    are query rows (positions len-prefill_rows .. len-1)
+    prefill_rows  : if > 0 (or a list, one entry per request), the last
+                    prefill_rows tokens of each request are query rows (positions
+                    len-n .. len-1), rows of one request contiguous
     lo_frac       : if > 0, per-(request, group) lower candidate bound drawn
                     uniformly in [0, lo_frac * n_blocks]
     """
@@ -121,11 +122,12 @@ def build_case(name, *, seed, ctx_lens, G, Hg, d_idx, k, D=128, n_idx=4, paged=T
         bt[r, :nblk[r]] = perm[off:off + nblk[r]].to(torch.int32)
         off += nblk[r]
     if prefill_rows:
-        assert R == 1
-        L = ctx_lens[0]
-        rows = prefill_rows
-        row_req = torch.zeros(rows, dtype=torch.int32)
-        row_pos = torch.arange(L - rows, L, dtype=torch.int32)
+        per = list(prefill_rows) if isinstance(prefill_rows, (list, tuple)) else [prefill_rows]
+        assert len(per) == R
+        row_req = torch.cat([torch.full((n,), r, dtype=torch.int32) for r, n in enumerate(per)])
+        row_pos = torch.cat([torch.arange(ctx_lens[r] - n, ctx_lens[r], dtype=torch.int32)
+                             for r, n in enumerate(per)])
+        rows = int(row_req.numel())
     else:
         rows = R
         row_req = torch.arange(R, dtype=torch.int32)

@@ -118,6 +118,21 @@ def test_prefill_hg4_ragged_tiles():
     pu.check_output(res["o"], res["lse"], o, lse)
 
 
+def test_prefill_several_requests():
+    """Rows of three requests in one call: row tiles that straddle requests,
+    request-specific pages and positions, through the tiled scorer and the
+    block-major kernel."""
+    print("[case] prefill 3 requests", flush=True)
+    case = _build(seed=203, ctx_lens=[2000, 900, 1500], G=2, Hg=8, d_idx=128, k=3,
+                  prefill_rows=[150, 200, 300], paged=True, lo_frac=0.2)
+    res = pu.gpu_path(case, prefill=True)
+    rows = list(range(case.rows))
+    _full_compare(case, res, rows)
+    op, lp, o, lse = pu.oracle_attn(case, rows, res["sel"].numpy(), res["pt"].numpy())
+    pu.check_partials(res["o_part"], res["lse_part"], op, lp)
+    pu.check_output(res["o"], res["lse"], o, lse)
+
+
 def test_deterministic_and_placement_invariant():
     """Two runs are bit-identical; moving pages in the pool (paged vs contiguous)
     and a token-major cache layout give bit-identical results."""
