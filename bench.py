@@ -139,12 +139,43 @@ def run_workload(cfg, steps, warmup, want_events=True):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
+    eager_ms = t0.elapsed_time(t1)
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
            for j, n in enumerate(names)}
+    o_ref, lse_ref = o.clone(), lse.clone()
+
+    # The same step captured once in a HIP graph and replayed: removes the
+    # host launch gaps between the five calls.  Every replay must reproduce the
+    # eager result bit for bit.
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()  # warm the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref)):
+        raise RuntimeError(f"{case.name}: graph replay differs from the eager step")
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record()
+    for _ in range(steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1)
+    if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref)):
+        raise RuntimeError(f"{case.name}: graph replay differs from the eager step")
     alg = algorithmic(case, sel)
-    return case, dict(total_ms=total_ms, ms_per_step=total_ms / steps, wall_s=wall,
-                      per_call_ms=per, alg=alg, sel=sel.cpu())
+    return case, dict(total_ms=graph_ms, ms_per_step=graph_ms / steps, eager_ms=eager_ms,
+                      eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per, alg=alg,
+                      sel=sel.cpu())
 
 
 def traffic_from_profile():
@@ -170,33 +201,47 @@ def cpu_baseline(case):
                 k_pool=bits(case.k_cache), v_pool=bits(case.v_cache))
     bt = case.block_table.cpu().numpy()
     pos = case.row_pos.cpu().numpy()
+    # repeat whole-batch passes until about 10 s of host work
     t = time.perf_counter()
-    oracle.decode_path(args["q_idx"], args["k_idx"], args["q"], args["k_pool"], args["v_pool"],
-                       bt, pos, case.k, case.nb, 1.0 / math.sqrt(case.D))
-    dt = time.perf_counter() - t
-    return dict(value=case.rows / dt, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
-                seconds=round(dt, 3),
-                sample=f"whole {case.name} batch ({case.rows} requests x {case.G} groups): "
-                       "index scores, top-k, page table, direct attention; fp64 C oracle")
+    passes = 0
+    while True:
+        oracle.decode_path(args["q_idx"], args["k_idx"], args["q"], args["k_pool"],
+                           args["v_pool"], bt, pos, case.k, case.nb, 1.0 / math.sqrt(case.D))
+        passes += 1
+        dt = time.perf_counter() - t
+        if dt >= 10.0 or passes >= 1000:
+            break
+    return dict(value=case.rows * passes / dt, unit="tok/s", cores=oracle.num_threads(),
+                kind="oracle", seconds=round(dt, 3),
+                sample=f"{passes} passes over the whole {case.name} batch ({case.rows} requests "
+                       f"x {case.G} groups): index scores, top-k, page table, direct attention; "
+                       "fp64 C oracle")
 
 
 def summarize(cfg, case, r):
     a = r["alg"]
     t = r["per_call_ms"]
     res = dict(workload=case.name, ms_per_step=round(r["ms_per_step"], 4),
+               eager_ms_per_step=round(r["eager_ms_per_step"], 4),
                per_call_us={k: round(v * 1e3, 2) for k, v in t.items()})
-    score_gbps = a["score_bytes"] / (t["index_score"] * 1e-3) / 1e9
-    res["index_score_GBps"] = round(score_gbps, 1)
-    res["index_score_hbm_frac"] = round(score_gbps / HBM_PEAK_GBPS, 4)
-    res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
-                                   ((t["index_score"] + t["topk"]) * 1e-3) / 1e9, 1)
+    if not case.prefill:
+        score_gbps = a["score_bytes"] / (t["index_score"] * 1e-3) / 1e9
+        res["index_score_GBps"] = round(score_gbps, 1)
+        res["index_score_hbm_frac"] = round(score_gbps / HBM_PEAK_GBPS, 4)
+        res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
+                                       ((t["index_score"] + t["topk"]) * 1e-3) / 1e9, 1)
     if case.prefill:
         res["attn_tflops_kernel_call"] = round(a["attn_flops"] / (t["attn"] * 1e-3) / 1e12, 2)
         res["attn_tflops_with_merge"] = round(a["attn_flops"] /
                                               ((t["attn"] + t["merge"]) * 1e-3) / 1e12, 2)
         res["attn_mfma_frac_call"] = round(res["attn_tflops_kernel_call"] / BF16_PEAK_TFLOPS, 4)
         res["attn_flops"] = a["attn_flops"]
-        res["index_tflops"] = round(a["index_flops"] / (t["index_score"] * 1e-3) / 1e12, 2)
+        # index scoring: the definition's FLOPs (every index vector separately) and
+        # the matrix-core FLOPs actually issued (qbar as bf16 hi + lo: 2 passes)
+        res["index_alg_tflops"] = round(a["index_flops"] / (t["index_score"] * 1e-3) / 1e12, 2)
+        mfma_flops = a["index_flops"] * 2 / case.n_idx
+        res["index_mfma_tflops"] = round(mfma_flops / (t["index_score"] * 1e-3) / 1e12, 2)
+        res["index_mfma_frac"] = round(res["index_mfma_tflops"] / BF16_PEAK_TFLOPS, 4)
     else:
         res["decode_tok_s"] = round(case.rows / (r["ms_per_step"] * 1e-3), 1)
         step_bytes = a["kidx"] + a["qidx"] + a["kv_bytes"] + a["qo_bytes"]
@@ -257,7 +302,9 @@ def main():
     value = main_case.rows * args.steps / (main_run["total_ms"] * 1e-3)
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tok/s", n_gpus=1, steps=args.steps,
-        warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4), higher_is_better=True,
+        warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4),
+        launch="hip graph replay of the five-call step (eager ms_per_step also reported)",
+        eager_ms_per_step=round(main_run["eager_ms_per_step"], 4), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=main_case.name, batch=main_case.rows,
                     context=int(main_case.ctx_len[0]), G=main_case.G, Hg=main_case.Hg,

@@ -33,15 +33,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 // Exclusive prefix count of `flag` over the workgroup in thread order; returns
 // the prefix for this thread and writes the workgroup total to *total.
+template <int NWAVES = kTopkWaves>
 __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int *total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t bal = __ballot(flag);
     const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+    if (NWAVES == 1) {
+        *total = __popcll(bal);
+        return in_wave;
+    }
     if (lane == 0) wave_tot[w] = __popcll(bal);
     __syncthreads();
     int before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkWaves; ++i) {
+    for (int i = 0; i < NWAVES; ++i) {
         const int c = wave_tot[i];
         before += (i < w) ? c : 0;
         tot += c;
@@ -49,6 +54,126 @@ __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int *t
     __syncthreads();
     *total = tot;
     return before + in_wave;
+}
+
+// Digit d of the current radix pass such that the keys above it number fewer
+// than `remain` and those at or above it at least `remain`; one wave scans the
+// 256-bin histogram (4 bins per lane, suffix sums from the top digit down).
+__device__ __forceinline__ void find_digit(const uint32_t *hist, int remain, int *digit,
+                                           int *above_out) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const int local = (int)(h0 + h1 + h2 + h3);
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_down(incl, off, kWave);
+        incl += (lane + off < kWave) ? v : 0;
+    }
+    int above = incl - local;  // keys in digits owned by higher lanes
+    const int hd[4] = {(int)h0, (int)h1, (int)h2, (int)h3};
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+        if (above < remain && remain <= above + hd[e]) {
+            *digit = 4 * lane + e;
+            *above_out = above;
+        }
+        above += hd[e];
+    }
+}
+
+// Register-resident variant: the scores of one (row, group) are read once into
+// KPT keys per thread (block b = i * THREADS + tid, so loads are coalesced and
+// the ordered pass walks b in ascending order); the radix passes then run on
+// registers with an LDS histogram.  THREADS = 64 needs no workgroup barrier
+// beyond the single wave's own.
+template <int THREADS, int KPT>
+__global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *__restrict__ scores,
+                                                           int score_stride,
+                                                           const int32_t *__restrict__ row_pos,
+                                                           int k, int32_t *__restrict__ sel) {
+    constexpr int NW = THREADS / kWave;
+    __shared__ uint32_t hist[256];
+    __shared__ int wave_tot[NW];
+    __shared__ int sh_digit, sh_above;
+    const int rg = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int own = row_pos[rg / G] / kBlk;
+    const float *s = scores + (int64_t)rg * score_stride;
+    int32_t *out = sel + (int64_t)rg * (k + 1);
+
+    // key 0 marks "not a candidate"; every finite score's key is > 0
+    uint32_t key[KPT];
+    int nvalid = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int b = i * THREADS + tid;
+        const float v = (b < own) ? s[b] : -INFINITY;
+        key[i] = (v != -INFINITY) ? order_key(v) : 0u;
+        nvalid += key[i] != 0u;
+    }
+    int ncand;
+    {
+        // workgroup sum of nvalid
+        int x = nvalid;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+        if (NW == 1) {
+            ncand = x;
+        } else {
+            if ((tid & 63) == 0) wave_tot[tid >> 6] = x;
+            __syncthreads();
+            ncand = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) ncand += wave_tot[i];
+            __syncthreads();
+        }
+    }
+
+    uint32_t thresh = 0u;
+    int take_eq = 0;
+    if (k == 0) {
+        thresh = 0xffffffffu;
+    } else if (k < ncand) {
+        uint32_t prefix = 0u, pmask = 0u;
+        int remain = k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += THREADS) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < KPT; ++i)
+                if (key[i] != 0u && (key[i] & pmask) == prefix)
+                    atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+            __syncthreads();
+            if (tid < kWave) find_digit(hist, remain, &sh_digit, &sh_above);
+            __syncthreads();
+            prefix |= (uint32_t)sh_digit << shift;
+            pmask |= 255u << shift;
+            remain -= sh_above;
+            __syncthreads();
+        }
+        thresh = prefix;
+        take_eq = remain;
+    }
+
+    int n_sel = 0, n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if (i * THREADS >= own) break;  // uniform
+        const int b = i * THREADS + tid;
+        const bool valid = key[i] != 0u;
+        const bool is_eq = valid && key[i] == thresh && take_eq > 0;
+        int eq_tot;
+        const int eq_rank = n_eq + block_excl_count<NW>(is_eq, wave_tot, &eq_tot);
+        const bool keep = valid && (key[i] > thresh || (is_eq && eq_rank < take_eq));
+        int keep_tot;
+        const int at = n_sel + block_excl_count<NW>(keep, wave_tot, &keep_tot);
+        if (keep) out[at] = b;
+        n_sel += keep_tot;
+        n_eq += eq_tot;
+    }
+    for (int i = n_sel + tid; i <= k; i += THREADS) out[i] = (i == n_sel) ? own : -1;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *__restrict__ scores,
@@ -61,7 +186,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
 
     const int rg = blockIdx.x;
     const int r = rg / G;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int own = row_pos[r] / kBlk;
     const float *s = scores + (int64_t)rg * score_stride;
     int32_t *out = sel + (int64_t)rg * (k + 1);
@@ -92,28 +217,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
                 if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
             }
             __syncthreads();
-            if (tid < kWave) {
-                // lane l owns digits 4l .. 4l+3; suffix sums from the top digit down
-                const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-                const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-                const int local = (int)(h0 + h1 + h2 + h3);
-                int incl = local;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) {
-                    const int v = __shfl_down(incl, off, kWave);
-                    incl += (lane + off < kWave) ? v : 0;
-                }
-                int above = incl - local;  // keys in digits owned by higher lanes
-                const int hd[4] = {(int)h0, (int)h1, (int)h2, (int)h3};
-#pragma unroll
-                for (int e = 3; e >= 0; --e) {
-                    if (above < remain && remain <= above + hd[e]) {
-                        sh_digit = 4 * lane + e;
-                        sh_above = above;
-                    }
-                    above += hd[e];
-                }
-            }
+            if (tid < kWave) find_digit(hist, remain, &sh_digit, &sh_above);
             __syncthreads();
             prefix |= (uint32_t)sh_digit << shift;
             pmask |= 255u << shift;
@@ -146,7 +250,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
         n_eq += eq_tot;
     }
     for (int i = n_sel + tid; i <= k; i += kTopkThreads) out[i] = (i == n_sel) ? own : -1;
-    (void)lane;
 }
 
 __global__ void page_table_kernel(int64_t n, int G, int nslot, const int32_t *__restrict__ sel,
@@ -165,9 +268,20 @@ __global__ void page_table_kernel(int64_t n, int G, int nslot, const int32_t *__
 
 hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
                        const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream) {
-    const int64_t pairs = (int64_t)rows * G;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)pairs), dim3(kTopkThreads), 0, stream, G,
-                       scores, score_stride, row_pos, k, sel);
+    const dim3 grid((unsigned)((int64_t)rows * G));
+    // scores per (row, group) held in registers: one wave up to 1024 blocks,
+    // a 256-thread workgroup up to 16384; beyond that the global-memory kernel
+#define MSA_TOPK_REG(T, K)                                                                  \
+    hipLaunchKernelGGL((topk_reg_kernel<T, K>), grid, dim3(T), 0, stream, G, scores,        \
+                       score_stride, row_pos, k, sel)
+    if (score_stride <= 64 * 8) MSA_TOPK_REG(64, 8);
+    else if (score_stride <= 64 * 16) MSA_TOPK_REG(64, 16);
+    else if (score_stride <= 256 * 16) MSA_TOPK_REG(256, 16);
+    else if (score_stride <= 256 * 32) MSA_TOPK_REG(256, 32);
+    else if (score_stride <= 256 * 64) MSA_TOPK_REG(256, 64);
+    else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, stream, G, scores,
+                            score_stride, row_pos, k, sel);
+#undef MSA_TOPK_REG
     return hipGetLastError();
 }
 

@@ -65,23 +65,28 @@ def test_small_decode_path(name):
     pu.check_output(res["o"], res["lse"], o, lse)
 
 
-def test_topk_exact_on_oracle_scores():
+@pytest.mark.parametrize("nb", [512, 700, 3000, 5000, 9000, 17000])
+def test_topk_exact_on_oracle_scores(nb):
     """Given identical fp32 scores the selection is integer work: bit-exact,
-    including exact ties (scores drawn from a few levels) and -inf holes."""
+    including exact ties (scores drawn from a few levels) and -inf holes.  The
+    block counts cover every kernel variant (one wave, one workgroup with 16, 32
+    or 64 keys per thread, and the global-memory fallback)."""
     import block_sparse_attention_09_amd as msa
-    print("[case] topk exact", flush=True)
-    rng = np.random.default_rng(9)
-    rows, G, nb = 37, 3, 700
+    print(f"[case] topk exact nb={nb}", flush=True)
+    rng = np.random.default_rng(9 + nb)
+    rows, G = (37, 3) if nb <= 3000 else (5, 2)
     levels = np.array([-2.0, -0.5, 0.0, 0.0, 0.25, 1.0, 3.0], np.float32)
     sc = rng.choice(levels, size=(rows, G, nb)).astype(np.float32)
     sc[::3] = rng.standard_normal((len(range(0, rows, 3)), G, nb)).astype(np.float32)
     sc[1, 1, :50] = -np.inf
-    sc[5, :, :] = -0.0
+    if rows > 5:
+        sc[5, :, :] = -0.0
     pos = rng.integers(0, nb * 128, size=rows).astype(np.int32)
     pos[0], pos[2] = 5, 130
-    for k in (0, 1, 7, 16, 33, 300, 800):
+    pos[3] = nb * 128 - 1
+    d = msa.Dims(G=G, Hg=1, D=128, n_idx=4, d_idx=128, blk=128)
+    for k in (0, 1, 7, 16, 33, 300, nb + 5):
         want = oracle.topk(sc, pos, k)
-        d = msa.Dims(G=G, Hg=1, D=128, n_idx=4, d_idx=128, blk=128)
         got = msa.msa_topk_blocks(d, torch.tensor(sc, device=DEV),
                                   torch.tensor(pos, device=DEV), k).cpu().numpy()
         assert np.array_equal(got, want), f"k={k}"
@@ -198,3 +203,64 @@ def test_empty_rows_is_noop():
     s = msa.msa_index_score(d, e, case.k_idx, case.block_table,
                             torch.empty(0, dtype=torch.int32, device=DEV), case.nb)
     assert s.shape == (0, 2, case.nb)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_graph_replay_matches_eager(prefill):
+    """The five-call step captured in a HIP graph: every replay (with eager work
+    and synchronisations in between) equals the eager result bit for bit."""
+    import block_sparse_attention_09_amd as msa
+    print(f"[case] graph replay prefill={prefill}", flush=True)
+    if prefill:
+        case = _build(seed=501, ctx_lens=[2500], G=2, Hg=8, d_idx=128, k=3, prefill_rows=400)
+    else:
+        case = _build(seed=502, ctx_lens=[3000, 2000, 900], G=2, Hg=4, d_idx=64, k=4)
+    d = pu.dims_of(case)
+    dev = case.q.device
+    scores = torch.empty((case.rows, case.G, case.nb), dtype=torch.float32, device=dev)
+    sel = torch.empty((case.rows, case.G, case.nslot), dtype=torch.int32, device=dev)
+    pt = torch.empty_like(sel)
+    o_part = torch.empty((case.rows, case.H, case.nslot, 128), dtype=torch.bfloat16, device=dev)
+    lse_part = torch.empty((case.rows, case.H, case.nslot), dtype=torch.float32, device=dev)
+    o = torch.empty((case.rows, case.H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.rows, case.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_prefill_workspace_size(d, case.rows, case.nslot, case.num_pages),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos, case.nb,
+                            row_req=case.row_req, num_reqs=case.num_reqs, scores=scores)
+        msa.msa_topk_blocks(d, scores, case.row_pos, case.k, sel=sel)
+        msa.msa_build_page_table(d, sel, case.block_table, row_req=case.row_req, page_table=pt)
+        if prefill:
+            msa.msa_sparse_attn_prefill(d, case.q, case.k_cache, case.v_cache, sel, pt,
+                                        case.row_pos, case.num_pages, workspace=ws,
+                                        o_part=o_part, lse_part=lse_part)
+        else:
+            msa.msa_sparse_attn_decode(d, case.q, case.k_cache, case.v_cache, sel, pt,
+                                       case.row_pos, o_part=o_part, lse_part=lse_part)
+        msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (scores, sel, pt, o_part, lse_part, o, lse)]
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        for t in (scores, o_part, o):
+            t.zero_()
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((scores, sel, pt, o_part, lse_part, o, lse), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
