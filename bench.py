@@ -47,8 +47,10 @@ def parse():
                     help="comma list of workload ids; the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run a plain 1-read/1-write device copy of this size "
-                         "(reference for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
+                    help="also run a plain 1-read/1-write fp32 elementwise kernel over this "
+                         "many MiB (reference for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time the eager step only (no graph capture), for counter runs")
     return ap.parse_args()
 
 
@@ -77,7 +79,7 @@ def algorithmic(case, sel=None):
     return out
 
 
-def run_workload(cfg, steps, warmup, want_events=True):
+def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
     import torch
     import block_sparse_attention_09_amd as msa
     import msa_synth
@@ -143,6 +145,11 @@ def run_workload(cfg, steps, warmup, want_events=True):
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
            for j, n in enumerate(names)}
     o_ref, lse_ref = o.clone(), lse.clone()
+    alg = algorithmic(case, sel)
+    if not graph_replay:
+        return case, dict(total_ms=eager_ms, ms_per_step=eager_ms / steps, eager_ms=eager_ms,
+                          eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
+                          alg=alg, sel=sel.cpu())
 
     # The same step captured once in a HIP graph and replayed: removes the
     # host launch gaps between the five calls.  Every replay must reproduce the
@@ -172,7 +179,6 @@ def run_workload(cfg, steps, warmup, want_events=True):
     graph_ms = g0.elapsed_time(g1)
     if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref)):
         raise RuntimeError(f"{case.name}: graph replay differs from the eager step")
-    alg = algorithmic(case, sel)
     return case, dict(total_ms=graph_ms, ms_per_step=graph_ms / steps, eager_ms=eager_ms,
                       eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per, alg=alg,
                       sel=sel.cpu())
@@ -271,7 +277,7 @@ def main():
     for cfg in order:
         steps = args.steps if cfg == main_cfg else max(5, min(args.steps, 20))
         print(f"[bench] workload {cfg}: {steps} steps", file=sys.stderr, flush=True)
-        case, r = run_workload(cfg, steps, args.warmup)
+        case, r = run_workload(cfg, steps, args.warmup, graph_replay=not args.eager_only)
         results[cfg] = summarize(cfg, case, r)
         if cfg == main_cfg:
             main_case, main_run = case, r
@@ -281,11 +287,13 @@ def main():
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src = torch.zeros(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
+        print(f"[bench] calibration: 3 x neg over {n} B read + {n} B written", file=sys.stderr,
+              flush=True)
 
     m = results[main_cfg]
     a = main_run["alg"]
@@ -303,14 +311,15 @@ def main():
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4),
-        launch="hip graph replay of the five-call step (eager ms_per_step also reported)",
+        launch=("eager five-call step" if args.eager_only else
+                "hip graph replay of the five-call step (eager ms_per_step also reported)"),
         eager_ms_per_step=round(main_run["eager_ms_per_step"], 4), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=main_case.name, batch=main_case.rows,
                     context=int(main_case.ctx_len[0]), G=main_case.G, Hg=main_case.Hg,
                     head_dim=main_case.D, n_idx=main_case.n_idx, d_idx=main_case.d_idx,
                     top_k=main_case.k, paged=True, parallelism="none (1 GPU)"),
-        index_scan_GBps=m["index_scan_GBps"], roofline=roofline, cpu_baseline=cpu,
+        index_scan_GBps=m.get("index_scan_GBps"), roofline=roofline, cpu_baseline=cpu,
         device=torch.cuda.get_device_name(0),
         workloads={results[c]["workload"]: results[c] for c in order})
     print(json.dumps(line))
