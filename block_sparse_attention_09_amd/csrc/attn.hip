@@ -55,28 +55,40 @@ __device__ __forceinline__ bf16x8 lds16(const bf16_t *p) {
 }
 
 // Stage one (page, group) of K and V into LDS.  128 tokens x 16 chunks of
-// 16 B per tensor; a wave reads 4 whole tokens (1 KB) per load.
-__device__ __forceinline__ void stage_kv(AttnSmem &sm, const bf16_t *kp, int64_t kts,
-                                         const bf16_t *vp, int64_t vts) {
-    const int tid = threadIdx.x;
+// 16 B per tensor; a wave reads 4 whole tokens (1 KB) per load.  The loads
+// are issued first (stage_kv_load) so other work can overlap their latency.
+struct KvStage {
     u32x4 kw[8], vw[8];
+};
+
+__device__ __forceinline__ void stage_kv_load(KvStage &st, const bf16_t *kp, int64_t kts,
+                                              const bf16_t *vp, int64_t vts) {
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = tid + kAttnThreads * i;
         const int t = c >> 4, d0 = (c & 15) * 8;
-        kw[i] = ld16(kp + (int64_t)t * kts + d0);
-        vw[i] = ld16(vp + (int64_t)t * vts + d0);
+        st.kw[i] = ld16(kp + (int64_t)t * kts + d0);
+        st.vw[i] = ld16(vp + (int64_t)t * vts + d0);
     }
+}
+
+// Writes the staged tiles; V rows of tokens past last_tok (seen by no query
+// of the unit, possibly never written) are stored as zeros, since a zero
+// softmax weight times a non-finite cache value would still poison P V.
+__device__ __forceinline__ void stage_kv_store(AttnSmem &sm, const KvStage &st, int last_tok) {
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = tid + kAttnThreads * i;
         const int t = c >> 4, d0 = (c & 15) * 8;
-        *reinterpret_cast<u32x4 *>(&sm.k[t * KST + d0]) = kw[i];
+        *reinterpret_cast<u32x4 *>(&sm.k[t * KST + d0]) = st.kw[i];
+        const u32x4 v = (t <= last_tok) ? st.vw[i] : u32x4{0u, 0u, 0u, 0u};
         bf16_t *col = &sm.vt[d0 * KST + vt_col(t)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            col[(2 * e) * KST] = (bf16_t)(vw[i][e] & 0xffffu);
-            col[(2 * e + 1) * KST] = (bf16_t)(vw[i][e] >> 16);
+            col[(2 * e) * KST] = (bf16_t)(v[e] & 0xffffu);
+            col[(2 * e + 1) * KST] = (bf16_t)(v[e] >> 16);
         }
     }
 }
@@ -348,47 +360,227 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_blockmajor_kernel(
     AttnArgs a, const int32_t *__restrict__ offs, const int32_t *__restrict__ list,
     float scale_log2) {
     __shared__ AttnSmem sm;
+    __shared__ int last_tok;
     const int64_t u = blockIdx.x;  // page * G + group
     const int o0 = offs[u], nq = offs[u + 1] - o0;
     if (nq == 0) return;
     const int g = (int)(u % a.G);
     const int64_t page = u / a.G;
-    stage_kv(sm, a.k + page * a.kps + (int64_t)g * a.kgs, a.kts,
-             a.v + page * a.vps + (int64_t)g * a.vgs, a.vts);
+    if (threadIdx.x == 0) last_tok = 0;
+    KvStage st;
+    stage_kv_load(st, a.k + page * a.kps + (int64_t)g * a.kgs, a.kts,
+                  a.v + page * a.vps + (int64_t)g * a.vgs, a.vts);
+    // the last token of the page that any query of the unit sees
+    int mine = 0;
+    for (int i = threadIdx.x; i < nq; i += kAttnThreads) {
+        const int e = list[o0 + i];
+        const int row = e / a.nslot, slot = e - row * a.nslot;
+        const int blk = a.sel[((int64_t)row * a.G + g) * a.nslot + slot];
+        mine = max(mine, min(kBlk - 1, a.row_pos[row] - blk * kBlk));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mine = max(mine, __shfl_xor(mine, m, kWave));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) atomicMax(&last_tok, mine);
+    __syncthreads();
+    stage_kv_store(sm, st, last_tok);
     __syncthreads();
     blockmajor_wave<HG>(sm, a, g, list + o0, nq, scale_log2);
 }
 
 // ------------------------------------------------------------------ decode
-// One workgroup per (row, group, slot): the selected page's K/V are staged in
-// LDS and wave 0 serves the row's Hg heads with the same per-wave code as the
-// block-major kernel (so both give bit-identical partials).
+// One workgroup per (row, group, slot); its four waves split the 128-token
+// block into 32-token slices, so every wave keeps loads in flight and the
+// workgroup holds 33 KB of LDS (four fit on a CU, enough for the whole
+// decode batch of a typical step to be resident at once).  Per wave:
+//   K slice    straight from global into the 16x16x32 A operands (16 tokens x
+//              32 dims per operand), non-temporal: each block is read once
+//   V slice    global -> LDS without a register round trip (16 B per lane,
+//              one 1 KB row group per instruction), then read back as V^T
+//              operands with the gfx950 transposing LDS read, so V is never
+//              scattered element by element
+//   S^T = K Q^T, softmax local to the slice, O^T = V^T P^T (fp32 accumulate)
+// and the four slices are combined in LDS the same way the final merge
+// combines blocks (local maxima rescaled to the common one).  Slices that lie
+// wholly past the row's position are neither loaded nor computed.
+constexpr int kDecThreads = 256;
+constexpr int kSlice = 32;             // tokens per wave
+constexpr int kCombStride = 132;       // fp32 per head in the combine area (bank padding)
+constexpr int kWaveLds = 16 * kCombStride * 4;  // bytes per wave: >= 32 x 256 B V slice
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v4i16x2 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Lanes 16 c .. 16 c + 15 each name 8 bytes (4 dims) of a 4-token x 16-dim
+// tile: lane s of the group points at token T0 + s / 4, dims D0 + 4 (s % 4).
+// The transposing read hands lane i of the group dim D0 + i of tokens
+// T0 .. T0 + 3 (element j = token T0 + j).
+__device__ __forceinline__ v4i16 lds_read_tr(const char *lds_byte_addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_byte_addr));
+}
+
 template <int HG>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_decode_kernel(AttnArgs a, float scale_log2) {
-    __shared__ AttnSmem sm;
-    __shared__ int32_t entry;
+__global__ __launch_bounds__(kDecThreads, 4) void attn_decode_kernel(AttnArgs a, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
+    __shared__ float wm[4][16], wl[4][16];
     const int unit = blockIdx.x;  // (r, g, s)
     const int s = unit % a.nslot;
     const int rg = unit / a.nslot;
     const int g = rg % a.G, r = rg / a.G;
     const int blk = a.sel[unit];
-    if (blk < 0) {
-        write_empty_slot<HG>(a, r, g, s, threadIdx.x, kAttnThreads);
+    const int pos = a.row_pos[r];
+    const int vis = pos - blk * kBlk;  // last visible token of the block
+    if (blk < 0 || vis < 0) {
+        write_empty_slot<HG>(a, r, g, s, threadIdx.x, kDecThreads);
         return;
     }
-    const int64_t page = a.page_table[unit];
-    if (threadIdx.x == 0) entry = r * a.nslot + s;
-    stage_kv(sm, a.k + page * a.kps + (int64_t)g * a.kgs, a.kts,
-             a.v + page * a.vps + (int64_t)g * a.vgs, a.vts);
+    const int H = a.G * HG;
+    const int nact = min(4, vis / kSlice + 1);  // waves with a visible token
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15, grp = lane >> 4;
+    char *wl_base = lds + w * kWaveLds;
+
+    if (w < nact) {
+        const int64_t page = a.page_table[unit];
+        const int tok0 = w * kSlice;
+        const bf16_t *kp = a.k + page * a.kps + (int64_t)g * a.kgs;
+        const bf16_t *vp = a.v + page * a.vps + (int64_t)g * a.vgs;
+        // V slice -> LDS, row-major [32 tokens][128 dims]: instruction i moves
+        // tokens 4 i .. 4 i + 3, lane l 16 bytes (token 4 i + l / 16, dims 8 (l % 16))
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(vp + (int64_t)(tok0 + 4 * i + grp) * a.vts + 8 * c16,
+                                             (lds_void *)(wl_base + 1024 * i), 16, 0, 0);
+        // K operands: [tt][ks] = K[tok0 + 16 tt + l % 16][32 ks + 8 (l / 16) ..]
+        bf16x8 kb[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kb[tt][ks] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    kp + (int64_t)(tok0 + 16 * tt + c16) * a.kts + 32 * ks + 8 * grp)));
+        // Q^T operands: head l % 16 (zero beyond Hg), dims 32 ks + 8 (l / 16) ..
+        bf16x8 qb[4];
+        const bf16_t *qp = a.q + ((int64_t)r * H + g * HG + (c16 < HG ? c16 : 0)) * 128 + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qb[ks] = (c16 < HG) ? as_bf16x8(ld16(qp + 32 * ks)) : bf16x8{};
+
+        // S^T tile tt: element i = token tok0 + 16 tt + 4 (l / 16) + i, head l % 16
+        f32x4 st[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) st[tt] = mfma16(kb[tt][ks], qb[ks], st[tt]);
+        float mx = -INFINITY;
+        if (vis >= tok0 + kSlice - 1) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[tt][i]);
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = tok0 + 16 * tt + 4 * grp + i;
+                    st[tt][i] = (tok <= vis) ? st[tt][i] : -INFINITY;
+                    mx = fmaxf(mx, st[tt][i]);
+                }
+        }
+        mx = wave_max_xor(mx, 16);
+        mx = wave_max_xor(mx, 32);  // finite: token tok0 is visible
+        const float off = -mx * scale_log2;
+        float p[8], l = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[4 * tt + i] = __builtin_amdgcn_exp2f(fmaf(st[tt][i], scale_log2, off));
+                l += p[4 * tt + i];
+            }
+        l = wave_sum_xor(l, 16);
+        l = wave_sum_xor(l, 32);
+        // P^T operand: K index 8 (l / 16) + i is token 4 (l / 16) + i of the slice,
+        // 8 (l / 16) + 4 + i is token 16 + 4 (l / 16) + i
+        u32x4 pw;
+        pw[0] = pack_bf16x2(p[0], p[1]);
+        pw[1] = pack_bf16x2(p[2], p[3]);
+        pw[2] = pack_bf16x2(p[4], p[5]);
+        pw[3] = pack_bf16x2(p[6], p[7]);
+        const bf16x8 pb = as_bf16x8(pw);
+
+        // the V slice has landed in LDS once this wave's loads are complete
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // masked tokens carry p = 0, but their cache rows may hold anything:
+        // rows past the last visible token are cleared before they are read
+        if (vis < tok0 + kSlice - 1) {
+            for (int t = vis - tok0 + 1; t < kSlice; ++t)
+                reinterpret_cast<uint32_t *>(wl_base + t * 256)[lane] = 0u;
+        }
+        // O^T tile dt: dims 16 dt + 4 (l / 16) + i, head l % 16
+        f32x4 ot[8];
+        const char *rd0 = wl_base + (4 * grp + (c16 >> 2)) * 256 + 8 * (c16 & 3);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const v4i16 lo = lds_read_tr(rd0 + 32 * dt);             // tokens 4 (l/16) + j
+            const v4i16 hi = lds_read_tr(rd0 + 16 * 256 + 32 * dt);  // tokens 16 + 4 (l/16) + j
+            const bf16x8 va = __builtin_bit_cast(
+                bf16x8, v4i16x2{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            ot[dt] = mfma16(va, pb, f32x4{});
+        }
+        // this wave's LDS now holds its un-normalised O^T, row max and sum
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (c16 < HG) {
+            float *cb = reinterpret_cast<float *>(wl_base) + c16 * kCombStride + 4 * grp;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(cb + 16 * dt) = ot[dt];
+            if (grp == 0) {
+                wm[w][c16] = mx;
+                wl[w][c16] = l;
+            }
+        }
+    }
     __syncthreads();
-    if ((threadIdx.x >> 6) == 0) blockmajor_wave<HG>(sm, a, g, &entry, 1, scale_log2);
+    // combine: thread t owns head t / 16, dims 8 (t % 16) .. + 8
+    const int t = threadIdx.x;
+    if (t < HG * 16) {
+        const int hh = t >> 4, c = t & 15;
+        float m = wm[0][hh];
+        for (int i = 1; i < nact; ++i) m = fmaxf(m, wm[i][hh]);
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float L = 0.f;
+        for (int i = 0; i < nact; ++i) {
+            const float f = __builtin_amdgcn_exp2f((wm[i][hh] - m) * scale_log2);
+            L += f * wl[i][hh];
+            const float *cb = reinterpret_cast<const float *>(lds + i * kWaveLds) +
+                              hh * kCombStride + 8 * c;
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(cb);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(cb + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += f * x0[e];
+                acc[4 + e] += f * x1[e];
+            }
+        }
+        const float inv = 1.f / L;
+        const int64_t oi = ((int64_t)r * H + g * HG + hh) * a.nslot + s;
+        u32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+        *reinterpret_cast<u32x4 *>(a.o_part + oi * 128 + 8 * c) = out;
+        if (c == 0) a.lse_part[oi] = (m * scale_log2 + __builtin_amdgcn_logf(L)) * kLn2;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream) {
     const float sl2 = a.sm_scale * kLog2e;
-    const dim3 grid((unsigned)((int64_t)a.rows * a.G * a.nslot)), block(kAttnThreads);
+    const dim3 grid((unsigned)((int64_t)a.rows * a.G * a.nslot)), block(kDecThreads);
     switch (a.Hg) {
         case 1: hipLaunchKernelGGL(attn_decode_kernel<1>, grid, block, 0, stream, a, sl2); break;
         case 2: hipLaunchKernelGGL(attn_decode_kernel<2>, grid, block, 0, stream, a, sl2); break;

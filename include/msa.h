@@ -174,8 +174,8 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const 
  * and the block loop runs outside the query loop; every KV block is moved from
  * HBM once and yields partial outputs that a log-sum-exp reduction combines.
  *
- * Same inputs and outputs as msa_sparse_attn_decode (the results are identical
- * to it row by row).  Internally it inverts sel into per-(group, page) query
+ * Same inputs and outputs as msa_sparse_attn_decode (the results agree with it
+ * up to fp32 summation order).  Internally it inverts sel into per-(group, page) query
  * lists in the workspace, then runs one pass per KV page that loads K and V
  * once and serves every (row, slot) that selected it.
  *

