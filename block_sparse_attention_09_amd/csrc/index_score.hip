@@ -23,6 +23,9 @@
 // HBM -> VGPR with no LDS round trip; B holds qbar hi/lo in column 0 only.
 #include "msa_internal.h"
 
+#include <algorithm>
+#include <atomic>
+
 namespace msa {
 
 namespace {
@@ -82,43 +85,44 @@ __device__ __forceinline__ float block_half_max(const StepBuf<DIDX> &buf, const 
     return best;
 }
 
+// Scored range of pair p = (row r, group g): blocks [slo, own], clamped to the
+// score row so that no index leaves the caller's buffers.
+struct PairInfo {
+    int r, g, req, pos, slo, n;  // n = own - slo + 1 scored blocks
+};
+
+__device__ __forceinline__ PairInfo pair_info(int p, int G, const int32_t *__restrict__ row_req,
+                                              const int32_t *__restrict__ row_pos,
+                                              const int32_t *__restrict__ blk_lo, int score_stride) {
+    PairInfo pi;
+    pi.r = p / G;
+    pi.g = p - pi.r * G;
+    pi.req = row_req ? row_req[pi.r] : pi.r;
+    pi.pos = row_pos[pi.r];
+    const int own = min(pi.pos / kBlk, score_stride - 1);
+    const int lo = blk_lo ? blk_lo[(int64_t)pi.req * G + pi.g] : 0;
+    pi.slo = max(0, lo < own ? lo : own);
+    pi.n = max(0, own - pi.slo + 1);
+    return pi;
+}
+
+// Scores of blocks [b_beg, b_end) of one (row, group), all inside its scored
+// range; at most kMaxChunk blocks (their pages are held one per lane).
 template <int DIDX>
-__global__ __launch_bounds__(256) void index_score_stream_kernel(
-    int rows, int G, int n_idx, const bf16_t *__restrict__ q_idx, const bf16_t *__restrict__ kbase,
-    int64_t kps, int64_t kgs, int64_t kts, const int32_t *__restrict__ block_table, int bt_stride,
-    const int32_t *__restrict__ row_req, const int32_t *__restrict__ row_pos,
-    const int32_t *__restrict__ blk_lo, float *__restrict__ scores, int score_stride, int cb,
-    int nchunk, float scale) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wave >= (int64_t)rows * G * nchunk) return;  // wave-uniform
-    const int chunk = (int)(wave % nchunk);
-    const int rg = (int)(wave / nchunk);
-    const int g = rg % G;
-    const int r = rg / G;
-    const int req = row_req ? row_req[r] : r;
-    const int pos = row_pos[r];
-    const int own = pos / kBlk;
-    const int lo = blk_lo ? blk_lo[(int64_t)req * G + g] : 0;
-    const int slo = lo < own ? lo : own;  // scored blocks: [slo, own]
-    const int b0 = chunk * cb;
-    const int b1 = min(b0 + cb, score_stride);
-    float *out = scores + ((int64_t)r * G + g) * score_stride;
-
-    // Blocks of the chunk outside the scored range get -inf.
-    const int s0 = max(b0, slo);
-    const int s1 = min(b1, own + 1);  // scored blocks of this chunk: [s0, s1)
-    for (int b = b0 + lane; b < b1; b += kWave)
-        if (b < s0 || b >= s1) out[b] = -INFINITY;
-    if (s0 >= s1) return;
-
-    // One round trip for everything the chunk needs besides the stream itself:
-    // the page of every scored block (one per lane) and the query index vectors.
-    const int32_t *bt = block_table + (int64_t)req * bt_stride;
-    const int my_page = (lane < s1 - s0) ? bt[s0 + lane] : 0;
+__device__ __forceinline__ void score_segment(const PairInfo &pi, int b_beg, int b_end, int n_idx,
+                                              int G, const bf16_t *__restrict__ q_idx,
+                                              const bf16_t *__restrict__ kbase, int64_t kps,
+                                              int64_t kgs, int64_t kts,
+                                              const int32_t *__restrict__ block_table,
+                                              int bt_stride, float *__restrict__ out, float scale,
+                                              int lane) {
+    const int32_t *bt = block_table + (int64_t)pi.req * bt_stride;
+    // the pages of the first (up to 64) blocks and the query index vectors in
+    // one round trip
+    const int my_page = (lane < b_end - b_beg) ? bt[b_beg + lane] : 0;
     const int kq = (lane >> 4) * 8;
     const bool col0 = (lane & 15) == 0;
-    const bf16_t *qb = q_idx + ((int64_t)r * G + g) * n_idx * DIDX + kq;
+    const bf16_t *qb = q_idx + ((int64_t)pi.r * G + pi.g) * n_idx * DIDX + kq;
     float acc[DIDX / 32][8];
 #pragma unroll
     for (int c = 0; c < DIDX / 32; ++c)
@@ -159,27 +163,98 @@ __global__ __launch_bounds__(256) void index_score_stream_kernel(
         blo[c] = as_bf16x8(lw);
     }
 
-    const int64_t gofs = (int64_t)g * kgs;
-    const int nblk = s1 - s0;
-    // Two register buffers, one per half block (static indices: no scratch).  The
-    // loads of the next half (or of the next block's page) are issued before the
-    // matrix-core work on the current half.
+    const int64_t gofs = (int64_t)pi.g * kgs;
+    const int nblk = b_end - b_beg;
+    // Two register buffers, one per half block (static indices: no scratch).
+    // The loads of the next half (or of the next block's page) are issued
+    // before the matrix-core work on the current half.
     StepBuf<DIDX> bufA, bufB;
     const bf16_t *page = kbase + (int64_t)__builtin_amdgcn_readlane(my_page, 0) * kps + gofs;
     load_step<DIDX>(bufA, page, kts, 0, lane);
     for (int bi = 0; bi < nblk; ++bi) {
-        const int tok_base = (s0 + bi) * kBlk + (lane >> 4) * 4;
+        const int tok_base = (b_beg + bi) * kBlk + (lane >> 4) * 4;
         load_step<DIDX>(bufB, page, kts, 1, lane);
-        float best = block_half_max<DIDX>(bufA, bhi, blo, tok_base, pos);
+        float best = block_half_max<DIDX>(bufA, bhi, blo, tok_base, pi.pos);
         if (bi + 1 < nblk) {
             page = kbase + (int64_t)__builtin_amdgcn_readlane(my_page, bi + 1) * kps + gofs;
             load_step<DIDX>(bufA, page, kts, 0, lane);
         }
-        best = fmaxf(best, block_half_max<DIDX>(bufB, bhi, blo, tok_base + 64, pos));
+        best = fmaxf(best, block_half_max<DIDX>(bufB, bhi, blo, tok_base + 64, pi.pos));
         // column 0 of the accumulators lives in lanes 0, 16, 32, 48
         best = wave_max_xor(best, 16);
         best = wave_max_xor(best, 32);
-        if (lane == 0) out[s0 + bi] = best * scale;
+        if (lane == 0) out[b_beg + bi] = best * scale;
+    }
+}
+
+// Balanced streaming: the scored blocks of all (row, group) pairs, in pair
+// order, are cut into nwaves equal slices, one per wave, so a ragged batch
+// ends with every wave finishing together instead of a tail of long rows.
+// Each wave first sums the pairs' block counts, then walks the pairs again
+// with a running prefix and scores the segments that fall in its slice.
+// Blocks outside a pair's scored range get -inf from wave p % nwaves.
+template <int DIDX>
+__global__ __launch_bounds__(256, 2) void index_score_stream_kernel(
+    int rows, int G, int n_idx, const bf16_t *__restrict__ q_idx, const bf16_t *__restrict__ kbase,
+    int64_t kps, int64_t kgs, int64_t kts, const int32_t *__restrict__ block_table, int bt_stride,
+    const int32_t *__restrict__ row_req, const int32_t *__restrict__ row_pos,
+    const int32_t *__restrict__ blk_lo, float *__restrict__ scores, int score_stride, int nwaves,
+    float scale) {
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= nwaves) return;  // wave-uniform
+    const int pairs = rows * G;
+
+    for (int p = w; p < pairs; p += nwaves) {
+        const PairInfo pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
+        float *out = scores + (int64_t)p * score_stride;
+        for (int b = lane; b < score_stride; b += kWave)
+            if (b < pi.slo || b >= pi.slo + pi.n) out[b] = -INFINITY;
+    }
+
+    int64_t total = 0;
+    for (int p0 = 0; p0 < pairs; p0 += kWave) {
+        const int p = p0 + lane;
+        int n = p < pairs ? pair_info(p, G, row_req, row_pos, blk_lo, score_stride).n : 0;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m, kWave);
+        total += n;
+    }
+    const int64_t beg = total * w / nwaves, end = total * (w + 1) / nwaves;
+    if (beg >= end) return;
+
+    int64_t base = 0;  // blocks of the pairs before this batch of 64
+    for (int p0 = 0; p0 < pairs && base < end; p0 += kWave) {
+        const int p = p0 + lane;
+        PairInfo pi = {0, 0, 0, 0, 0, 0};
+        if (p < pairs) pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
+        int incl = pi.n;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off, kWave);
+            incl += (lane >= off) ? v : 0;
+        }
+        const int64_t start = base + incl - pi.n;
+        uint64_t hits = __ballot(pi.n > 0 && start < end && start + pi.n > beg);
+        while (hits) {
+            const int l = __builtin_ctzll(hits);
+            hits &= hits - 1;
+            PairInfo q;
+            q.r = __shfl(pi.r, l, kWave);
+            q.g = __shfl(pi.g, l, kWave);
+            q.req = __shfl(pi.req, l, kWave);
+            q.pos = __shfl(pi.pos, l, kWave);
+            q.slo = __shfl(pi.slo, l, kWave);
+            q.n = __shfl(pi.n, l, kWave);
+            const int64_t st = base + __shfl(incl, l, kWave) - q.n;
+            const int b_beg = q.slo + (int)max((int64_t)0, beg - st);
+            const int b_end = q.slo + (int)min((int64_t)q.n, end - st);
+            for (int c0 = b_beg; c0 < b_end; c0 += kMaxChunk)
+                score_segment<DIDX>(q, c0, min(c0 + kMaxChunk, b_end), n_idx, G, q_idx, kbase, kps,
+                                    kgs, kts, block_table, bt_stride,
+                                    scores + ((int64_t)q.r * G + q.g) * score_stride, scale, lane);
+        }
+        base += __shfl(incl, kWave - 1, kWave);
     }
 }
 
@@ -428,27 +503,39 @@ hipError_t launch_index_score(const msa_dims_t &d, int rows, const bf16_t *q_idx
                                scores, score_stride, scale);
         return hipGetLastError();
     }
-    // Chunk length: enough waves to fill 256 CUs several times over.
+    // One wave per resident wave slot of the device (the balanced kernel is
+    // meant to run in a single round), but no more than one per 4 blocks.
+    static std::atomic<int> resident_waves[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) dev = 0;
+    if (resident_waves[dev].load(std::memory_order_relaxed) == 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = d.d_idx == 128
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_score_stream_kernel<128>, 256, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_score_stream_kernel<64>, 256, 0);
+        if (e != hipSuccess) return e;
+        resident_waves[dev].store((cus > 0 && per_cu > 0) ? cus * per_cu * 4 : 4096,
+                                  std::memory_order_relaxed);
+    }
     const int64_t pairs = (int64_t)rows * d.G;
-#ifndef MSA_SCORE_WAVES_TARGET
-#define MSA_SCORE_WAVES_TARGET 4096
-#endif
-    int cb = (int)((pairs * score_stride) / MSA_SCORE_WAVES_TARGET);
-    cb = cb < 2 ? 2 : (cb > 16 ? 16 : cb);
-    static_assert(16 <= kMaxChunk, "chunk pages are held one per lane");
-    const int nchunk = (score_stride + cb - 1) / cb;
-    const int64_t waves = pairs * nchunk;
-    const int64_t blocks = (waves + 3) / 4;
+    const int64_t ub = pairs * score_stride;  // scored blocks, upper bound
+    const int nwaves = (int)std::max<int64_t>(
+        1, std::min<int64_t>(resident_waves[dev].load(std::memory_order_relaxed), (ub + 3) / 4));
+    const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
     if (d.d_idx == 128)
-        hipLaunchKernelGGL(index_score_stream_kernel<128>, dim3((unsigned)blocks), dim3(256), 0,
-                           stream, rows, d.G, d.n_idx, q_idx, kb, kv.page_stride,
-                           kv.group_stride, kv.token_stride, block_table, bt_stride, row_req,
-                           row_pos, blk_lo, scores, score_stride, cb, nchunk, scale);
+        hipLaunchKernelGGL(index_score_stream_kernel<128>, grid, block, 0, stream, rows, d.G,
+                           d.n_idx, q_idx, kb, kv.page_stride, kv.group_stride, kv.token_stride,
+                           block_table, bt_stride, row_req, row_pos, blk_lo, scores, score_stride,
+                           nwaves, scale);
     else
-        hipLaunchKernelGGL(index_score_stream_kernel<64>, dim3((unsigned)blocks), dim3(256), 0,
-                           stream, rows, d.G, d.n_idx, q_idx, kb, kv.page_stride,
-                           kv.group_stride, kv.token_stride, block_table, bt_stride, row_req,
-                           row_pos, blk_lo, scores, score_stride, cb, nchunk, scale);
+        hipLaunchKernelGGL(index_score_stream_kernel<64>, grid, block, 0, stream, rows, d.G,
+                           d.n_idx, q_idx, kb, kv.page_stride, kv.group_stride, kv.token_stride,
+                           block_table, bt_stride, row_req, row_pos, blk_lo, scores, score_stride,
+                           nwaves, scale);
     return hipGetLastError();
 }
 
