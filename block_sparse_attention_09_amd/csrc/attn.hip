@@ -391,8 +391,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_blockmajor_kernel(
 // ------------------------------------------------------------------ decode
 // One workgroup per (row, group, slot); its four waves split the 128-token
 // block into 32-token slices, so every wave keeps loads in flight and the
-// workgroup holds 33 KB of LDS (four fit on a CU, enough for the whole
-// decode batch of a typical step to be resident at once).  Per wave:
+// workgroup holds 32 KB of LDS (five fit on a CU: 1,280 resident units, a
+// whole 8-row x 8-group x 17-slot decode step in one round).  Per wave:
 //   K slice    straight from global into the 16x16x32 A operands (16 tokens x
 //              32 dims per operand), non-temporal: each block is read once
 //   V slice    global -> LDS without a register round trip (16 B per lane,
@@ -405,8 +405,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_blockmajor_kernel(
 // wholly past the row's position are neither loaded nor computed.
 constexpr int kDecThreads = 256;
 constexpr int kSlice = 32;             // tokens per wave
-constexpr int kCombStride = 132;       // fp32 per head in the combine area (bank padding)
-constexpr int kWaveLds = 16 * kCombStride * 4;  // bytes per wave: >= 32 x 256 B V slice
+constexpr int kWaveLds = kSlice * 256;  // bytes per wave: its 32 x 256 B V slice
+// After its P V a wave reuses its slice for the combine: un-normalised O^T as
+// fp32 [head][dim] rows of comb_stride floats, then its row maxima and sums.
+// With Hg <= 8 everything fits in the slice (32 KB of LDS per workgroup, five
+// workgroups per CU); Hg = 16 keeps maxima and sums in a separate array.
+template <int HG>
+struct DecComb {
+    static constexpr int stride = HG <= 8 ? 132 : 128;  // fp32; 132 spreads heads over banks
+    static constexpr int ml_ofs = HG * stride * 4;      // byte offset of maxima, then sums
+    static constexpr bool ml_in_slice = ml_ofs + 2 * 16 * 4 <= kWaveLds;
+};
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v4i16x2 __attribute__((ext_vector_type(8)));
@@ -422,9 +431,21 @@ __device__ __forceinline__ v4i16 lds_read_tr(const char *lds_byte_addr) {
 }
 
 template <int HG>
-__global__ __launch_bounds__(kDecThreads, 4) void attn_decode_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(kDecThreads, 5) void attn_decode_kernel(AttnArgs a, float scale_log2) {
     __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
-    __shared__ float wm[4][16], wl[4][16];
+    using C = DecComb<HG>;
+    // maxima and sums of wave i: ml(i)[0 .. 15] and ml(i)[16 .. 31]
+    float *ml_extra = nullptr;
+    if constexpr (!C::ml_in_slice) {
+        __shared__ float ml_sep[4][32];
+        ml_extra = &ml_sep[0][0];
+    }
+    auto ml = [&](int i) -> float * {
+        if constexpr (C::ml_in_slice)
+            return reinterpret_cast<float *>(lds + i * kWaveLds + C::ml_ofs);
+        else
+            return ml_extra + 32 * i;
+    };
     const int unit = blockIdx.x;  // (r, g, s)
     const int s = unit % a.nslot;
     const int rg = unit / a.nslot;
@@ -535,12 +556,12 @@ __global__ __launch_bounds__(kDecThreads, 4) void attn_decode_kernel(AttnArgs a,
         // this wave's LDS now holds its un-normalised O^T, row max and sum
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (c16 < HG) {
-            float *cb = reinterpret_cast<float *>(wl_base) + c16 * kCombStride + 4 * grp;
+            float *cb = reinterpret_cast<float *>(wl_base) + c16 * C::stride + 4 * grp;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(cb + 16 * dt) = ot[dt];
             if (grp == 0) {
-                wm[w][c16] = mx;
-                wl[w][c16] = l;
+                ml(w)[c16] = mx;
+                ml(w)[16 + c16] = l;
             }
         }
     }
@@ -549,15 +570,15 @@ __global__ __launch_bounds__(kDecThreads, 4) void attn_decode_kernel(AttnArgs a,
     const int t = threadIdx.x;
     if (t < HG * 16) {
         const int hh = t >> 4, c = t & 15;
-        float m = wm[0][hh];
-        for (int i = 1; i < nact; ++i) m = fmaxf(m, wm[i][hh]);
+        float m = ml(0)[hh];
+        for (int i = 1; i < nact; ++i) m = fmaxf(m, ml(i)[hh]);
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         float L = 0.f;
         for (int i = 0; i < nact; ++i) {
-            const float f = __builtin_amdgcn_exp2f((wm[i][hh] - m) * scale_log2);
-            L += f * wl[i][hh];
+            const float f = __builtin_amdgcn_exp2f((ml(i)[hh] - m) * scale_log2);
+            L += f * ml(i)[16 + hh];
             const float *cb = reinterpret_cast<const float *>(lds + i * kWaveLds) +
-                              hh * kCombStride + 8 * c;
+                              hh * C::stride + 8 * c;
             const f32x4 x0 = *reinterpret_cast<const f32x4 *>(cb);
             const f32x4 x1 = *reinterpret_cast<const f32x4 *>(cb + 4);
 #pragma unroll
