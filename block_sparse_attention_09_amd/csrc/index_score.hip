@@ -192,7 +192,8 @@ __device__ __forceinline__ void score_segment(const PairInfo &pi, int b_beg, int
 // ends with every wave finishing together instead of a tail of long rows.
 // Each wave first sums the pairs' block counts, then walks the pairs again
 // with a running prefix and scores the segments that fall in its slice.
-// Blocks outside a pair's scored range get -inf from wave p % nwaves.
+// Blocks outside a pair's scored range get -inf from wave p % nwaves.  With
+// up to 64 pairs everything the stream needs arrives in one round trip.
 template <int DIDX>
 __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(
     int rows, int G, int n_idx, const bf16_t *__restrict__ q_idx, const bf16_t *__restrict__ kbase,
@@ -205,20 +206,36 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(
     if (w >= nwaves) return;  // wave-uniform
     const int pairs = rows * G;
 
-    for (int p = w; p < pairs; p += nwaves) {
-        const PairInfo pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
-        float *out = scores + (int64_t)p * score_stride;
-        for (int b = lane; b < score_stride; b += kWave)
-            if (b < pi.slo || b >= pi.slo + pi.n) out[b] = -INFINITY;
-    }
-
+    // The first 64 pairs' metadata is kept from the counting pass, so a batch
+    // of up to 64 pairs costs one round trip before the stream starts.
+    // Pair w's range (for its -inf fill) is picked up on the way as well.
     int64_t total = 0;
+    PairInfo first = {0, 0, 0, 0, 0, 0};
+    int fill_slo = 0, fill_n = 0;
     for (int p0 = 0; p0 < pairs; p0 += kWave) {
         const int p = p0 + lane;
-        int n = p < pairs ? pair_info(p, G, row_req, row_pos, blk_lo, score_stride).n : 0;
+        PairInfo pi = {0, 0, 0, 0, 0, 0};
+        if (p < pairs) pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
+        if (p0 == 0) first = pi;
+        if (p0 == (w & ~(kWave - 1))) {
+            fill_slo = __shfl(pi.slo, w & (kWave - 1), kWave);
+            fill_n = __shfl(pi.n, w & (kWave - 1), kWave);
+        }
+        int n = pi.n;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m, kWave);
         total += n;
+    }
+    // -inf for the blocks outside the scored ranges of pairs w, w + nwaves, ...
+    for (int p = w; p < pairs; p += nwaves) {
+        if (p != w) {
+            const PairInfo pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
+            fill_slo = pi.slo;
+            fill_n = pi.n;
+        }
+        float *out = scores + (int64_t)p * score_stride;
+        for (int b = lane; b < score_stride; b += kWave)
+            if (b < fill_slo || b >= fill_slo + fill_n) out[b] = -INFINITY;
     }
     const int64_t beg = total * w / nwaves, end = total * (w + 1) / nwaves;
     if (beg >= end) return;
@@ -226,8 +243,11 @@ __global__ __launch_bounds__(256, 2) void index_score_stream_kernel(
     int64_t base = 0;  // blocks of the pairs before this batch of 64
     for (int p0 = 0; p0 < pairs && base < end; p0 += kWave) {
         const int p = p0 + lane;
-        PairInfo pi = {0, 0, 0, 0, 0, 0};
-        if (p < pairs) pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
+        PairInfo pi = first;
+        if (p0 != 0) {
+            pi = PairInfo{0, 0, 0, 0, 0, 0};
+            if (p < pairs) pi = pair_info(p, G, row_req, row_pos, blk_lo, score_stride);
+        }
         int incl = pi.n;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
