@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void index_score_tiled_kernel(
     constexpr int LD_PER_THREAD = kBlk * DIDX / 8 / 256;   // 16-B loads per thread per block
     __shared__ __attribute__((aligned(16))) bf16_t kbuf[2][kBlk * KST];
     __shared__ int s_req[kTileRows], s_pos[kTileRows], s_slo[kTileRows];
-    __shared__ int s_run[3];  // current request, first block, last block
+    __shared__ int s_run[5];  // request, first and last block, unmasked block range
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = blockIdx.x % G;
@@ -390,21 +390,31 @@ __global__ __launch_bounds__(256, 2) void index_score_tiled_kernel(
     int done_upto = 0;  // runs are found in row order
     for (;;) {
         if (tid == 0) {
-            int req = -1, blo_ = 0x7fffffff, bhi_ = -1;
+            // the run's request, its block range, and the blocks [full_lo,
+            // full_hi) that every row of the tile scores with all 128 tokens
+            // visible (the common case: no mask needed there)
+            int req = -1, blo_ = 0x7fffffff, bhi_ = -1, n_in = 0;
+            int full_lo = 0, full_hi = 0x7fffffff;
             for (int i = 0; i < nrows; ++i) {
                 if (s_req[i] < 0) continue;   // already served
                 if (req < 0) req = s_req[i];
                 if (s_req[i] == req) {
                     blo_ = min(blo_, s_slo[i]);
                     bhi_ = max(bhi_, s_pos[i] / kBlk);
+                    full_lo = max(full_lo, s_slo[i]);
+                    full_hi = min(full_hi, (s_pos[i] + 1) / kBlk);  // blocks < this are whole
+                    ++n_in;
                 }
             }
             s_run[0] = req;
             s_run[1] = blo_;
             s_run[2] = bhi_;
+            s_run[3] = (n_in == kTileRows) ? full_lo : 0;
+            s_run[4] = (n_in == kTileRows) ? full_hi : 0;
         }
         __syncthreads();
         const int req = s_run[0], b_first = s_run[1], b_last = s_run[2];
+        const int full_lo = s_run[3], full_hi = s_run[4];
         if (req < 0) break;
         (void)done_upto;
         const int32_t *bt = block_table + (int64_t)req * bt_stride;
@@ -453,25 +463,47 @@ __global__ __launch_bounds__(256, 2) void index_score_tiled_kernel(
                                                                         : -1;
             float best[2] = {-INFINITY, -INFINITY};
             const bf16_t *kb = &kbuf[cur][0];
+            if (b >= full_lo && b < full_hi) {
+                // every row sees the whole block: plain maxima
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                bf16x8 a[NC];
+                for (int mt = 0; mt < 8; ++mt) {
+                    bf16x8 a[NC];
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    a[c] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                        kb + (16 * mt + (lane & 15)) * KST + 32 * c + kq));
+                    for (int c = 0; c < NC; ++c)
+                        a[c] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                            kb + (16 * mt + (lane & 15)) * KST + 32 * c + kq));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                    for (int nt = 0; nt < 2; ++nt) {
+                        f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int c = 0; c < NC; ++c) {
-                        d = mfma16(a[c], bhi[nt][c], d);
-                        d = mfma16(a[c], blo[nt][c], d);
+                        for (int c = 0; c < NC; ++c) {
+                            d = mfma16(a[c], bhi[nt][c], d);
+                            d = mfma16(a[c], blo[nt][c], d);
+                        }
+                        best[nt] = fmaxf(best[nt], fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3])));
                     }
-                    const int t0 = 16 * mt + (lane >> 4) * 4;
+                }
+            } else {
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        best[nt] = fmaxf(best[nt], (t0 + ii <= lim[nt]) ? d[ii] : -INFINITY);
+                for (int mt = 0; mt < 8; ++mt) {
+                    bf16x8 a[NC];
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+                        a[c] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                            kb + (16 * mt + (lane & 15)) * KST + 32 * c + kq));
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) {
+                            d = mfma16(a[c], bhi[nt][c], d);
+                            d = mfma16(a[c], blo[nt][c], d);
+                        }
+                        const int t0 = 16 * mt + (lane >> 4) * 4;
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            best[nt] = fmaxf(best[nt], (t0 + ii <= lim[nt]) ? d[ii] : -INFINITY);
+                    }
                 }
             }
 #pragma unroll
