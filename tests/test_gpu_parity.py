@@ -38,6 +38,13 @@ SMALL = {
     # cache slots past each request's last token hold NaN: nothing may leak
     "nan-tail": dict(seed=108, ctx_lens=[700, 1000, 2049, 33], G=2, Hg=8, d_idx=128, k=3,
                      poison="nan"),
+    # lower bounds drawn up to 1.5x the block count: some groups score only their own block
+    "lo-above-own": dict(seed=109, ctx_lens=[900, 1400, 2000], G=2, Hg=4, d_idx=64, k=3,
+                         lo_frac=1.5),
+    # 3,000 (row, group) pairs of 3 blocks: more pairs than the scan has waves, so
+    # waves fill several pairs' -inf ranges and slices cross many pair boundaries
+    "many-pairs": dict(seed=110, ctx_lens=[300 + (i % 7) * 13 for i in range(1000)], G=3, Hg=2,
+                       d_idx=64, k=2),
 }
 
 
@@ -133,6 +140,33 @@ def test_prefill_nan_tail():
     print("[case] prefill nan tail", flush=True)
     case = _build(seed=204, ctx_lens=[1500, 700], G=2, Hg=8, d_idx=128, k=3,
                   prefill_rows=[300, 90], paged=True, poison="nan")
+    res = pu.gpu_path(case, prefill=True)
+    rows = list(range(case.rows))
+    _full_compare(case, res, rows)
+    op, lp, o, lse = pu.oracle_attn(case, rows, res["sel"].numpy(), res["pt"].numpy())
+    pu.check_partials(res["o_part"], res["lse_part"], op, lp)
+    pu.check_output(res["o"], res["lse"], o, lse)
+
+
+PREFILL_SHAPES = {
+    # Hg 1 / 2 / 16 exercise the other block-major tile shapes (32 / 16 / 2 query
+    # tokens per 32-row tile); n_idx 1 / 7 / 16 the scorer's index-vector loop
+    "hg1-nidx1": dict(seed=205, ctx_lens=[1300], G=2, Hg=1, d_idx=128, k=3, n_idx=1,
+                      prefill_rows=257),
+    "hg2-nidx7-d64": dict(seed=206, ctx_lens=[1100], G=3, Hg=2, d_idx=64, k=4, n_idx=7,
+                          prefill_rows=190),
+    "hg16-nidx16": dict(seed=207, ctx_lens=[900], G=1, Hg=16, d_idx=128, k=2, n_idx=16,
+                        prefill_rows=140),
+    # only the own block, and every earlier block
+    "k0": dict(seed=208, ctx_lens=[1000], G=2, Hg=8, d_idx=64, k=0, prefill_rows=200),
+    "k-all": dict(seed=209, ctx_lens=[1000], G=2, Hg=8, d_idx=64, k=50, prefill_rows=200),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_SHAPES))
+def test_prefill_shapes(name):
+    print(f"[case] prefill {name}", flush=True)
+    case = _build(paged=True, **PREFILL_SHAPES[name])
     res = pu.gpu_path(case, prefill=True)
     rows = list(range(case.rows))
     _full_compare(case, res, rows)
