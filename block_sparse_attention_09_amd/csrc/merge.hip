@@ -19,50 +19,55 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// One wave serves four (row, head) pairs; 16 lanes per pair, 8 dims each.
-// Slots go in batches of 8 with all their loads issued together, so a short
-// merge (decode: a few hundred pairs) costs a few memory round trips rather
-// than one per slot.
-constexpr int kBatch = 8;
+// 16 lanes own one (row, head) pair, 8 dims (16 B) each; a 256-thread
+// workgroup serves 16 pairs.  Slots go in batches of kBatch (one batch holds a
+// top-16 + own selection) with every load of a batch -- the batch's LSEs and
+// all its partial rows -- issued before any is used, so a pair costs one
+// memory round trip per batch; batches are combined with a running maximum.
+// An empty slot (lse = -inf) gets weight 0 and its row is excluded by a
+// select, so whatever that row holds never reaches the result.
+constexpr int kBatch = 17;
+constexpr int kMergeThreads = 256;
 
-__global__ __launch_bounds__(64) void lse_merge_kernel(int64_t pairs, int nslot,
-                                                       const bf16_t *__restrict__ o_part,
-                                                       const float *__restrict__ lse_part,
-                                                       bf16_t *__restrict__ o,
-                                                       float *__restrict__ lse) {
-    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 4);
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(int64_t pairs, int nslot,
+                                                                  const bf16_t *__restrict__ o_part,
+                                                                  const float *__restrict__ lse_part,
+                                                                  bf16_t *__restrict__ o,
+                                                                  float *__restrict__ lse) {
+    const int64_t pair = (int64_t)blockIdx.x * (kMergeThreads / 16) + (threadIdx.x >> 4);
     const int sub = threadIdx.x & 15;
-    if (pair >= pairs) return;
+    if (pair >= pairs) return;  // whole 16-lane groups leave together
     const float *ls = lse_part + pair * nslot;
     const bf16_t *op = o_part + pair * nslot * 128 + sub * 8;
-    float m = -INFINITY;
+    float m = -INFINITY, wsum = 0.f;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int s0 = 0; s0 < nslot; s0 += kBatch) {
         float l[kBatch];
+        u32x4 v[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) l[i] = (s0 + i < nslot) ? ls[s0 + i] : -INFINITY;
+        for (int i = 0; i < kBatch; ++i) {
+            const bool in = s0 + i < nslot;
+            l[i] = in ? ls[s0 + i] : -INFINITY;
+            v[i] = in ? ld16(op + (int64_t)(s0 + i) * 128) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float mb = m;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) m = fmaxf(m, l[i]);
-    }
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float wsum = 0.f;
-    if (m != -INFINITY) {
-        for (int s0 = 0; s0 < nslot; s0 += kBatch) {
-            float l[kBatch];
-            u32x4 v[kBatch];
+        for (int i = 0; i < kBatch; ++i) mb = fmaxf(mb, l[i]);
+        if (mb == -INFINITY) continue;  // nothing valid yet
+        const float rescale = __builtin_amdgcn_exp2f((m - mb) * kLog2e);  // 0 when m = -inf
+        wsum *= rescale;
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) l[i] = (s0 + i < nslot) ? ls[s0 + i] : -INFINITY;
+        for (int e = 0; e < 8; ++e) acc[e] *= rescale;
+        m = mb;
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i)  // empty slots (lse = -inf) are never read
-                v[i] = (l[i] != -INFINITY) ? ld16(op + (int64_t)(s0 + i) * 128) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < kBatch; ++i) {
+            const bool use = l[i] != -INFINITY;
+            const float w = use ? __builtin_amdgcn_exp2f((l[i] - m) * kLog2e) : 0.f;
+            wsum += w;
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const float w = __builtin_amdgcn_exp2f((l[i] - m) * kLog2e);  // 0 for empty
-                wsum += w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += w * bf16_lo(v[i][e]);
-                    acc[2 * e + 1] += w * bf16_hi(v[i][e]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += use ? w * bf16_lo(v[i][e]) : 0.f;
+                acc[2 * e + 1] += use ? w * bf16_hi(v[i][e]) : 0.f;
             }
         }
     }
@@ -84,8 +89,9 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(int64_t pairs, int nslot,
 hipError_t launch_lse_merge(int rows, int H, int nslot, const bf16_t *o_part,
                             const float *lse_part, bf16_t *o, float *lse, hipStream_t stream) {
     const int64_t pairs = (int64_t)rows * H;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(64), 0, stream,
-                       pairs, nslot, o_part, lse_part, o, lse);
+    const int64_t per_wg = kMergeThreads / 16;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((pairs + per_wg - 1) / per_wg)),
+                       dim3(kMergeThreads), 0, stream, pairs, nslot, o_part, lse_part, o, lse);
     return hipGetLastError();
 }
 
