@@ -2,9 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workloads 2,5,3,4,1]
 
-A step is one pass of the whole path over one batch: index scores, top-k, page
-table, sparse attention (decode kernel, or the KV-block-major prefill), LSE
-merge.  The headline line is the decode workload at 64K context, batch 8
+A step is one pass of the whole path over one batch: index scores, top-k with
+the page table (msa_topk_blocks_paged: one kernel writes both), sparse attention
+(decode kernel, or the KV-block-major prefill), LSE merge.  The headline line is the decode workload at 64K context, batch 8
 (8 KV groups x 8 heads, d_idx 128, top-16 + own block, paged):
 value = decode tokens/s of one MSA layer = batch x steps / time.
 
@@ -101,7 +101,7 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
     if case.prefill:
         nbytes = msa.msa_prefill_workspace_size(d, case.rows, case.nslot, case.num_pages)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    names = ["index_score", "topk", "page_table", "attn", "merge"]
+    names = ["index_score", "topk_page_table", "attn", "merge"]
 
     def step(ev=None):
         def mark(i):
@@ -112,10 +112,9 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
                             row_req=case.row_req, blk_lo=case.blk_lo, num_reqs=case.num_reqs,
                             scores=scores)
         mark(1)
-        msa.msa_topk_blocks(d, scores, case.row_pos, case.k, sel=sel)
+        msa.msa_topk_blocks_paged(d, scores, case.row_pos, case.k, case.block_table,
+                                  row_req=case.row_req, sel=sel, page_table=pt)
         mark(2)
-        msa.msa_build_page_table(d, sel, case.block_table, row_req=case.row_req, page_table=pt)
-        mark(3)
         if case.prefill:
             msa.msa_sparse_attn_prefill(d, case.q, case.k_cache, case.v_cache, sel, pt,
                                         case.row_pos, case.num_pages, scale, workspace=ws,
@@ -123,14 +122,15 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
         else:
             msa.msa_sparse_attn_decode(d, case.q, case.k_cache, case.v_cache, sel, pt,
                                        case.row_pos, scale, o_part=o_part, lse_part=lse_part)
-        mark(4)
+        mark(3)
         msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
-        mark(5)
+        mark(4)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -152,7 +152,7 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
                           alg=alg, sel=sel.cpu())
 
     # The same step captured once in a HIP graph and replayed: removes the
-    # host launch gaps between the five calls.  Every replay must reproduce the
+    # host launch gaps between the calls.  Every replay must reproduce the
     # eager result bit for bit.
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
@@ -235,7 +235,7 @@ def summarize(cfg, case, r):
         res["index_score_GBps"] = round(score_gbps, 1)
         res["index_score_hbm_frac"] = round(score_gbps / HBM_PEAK_GBPS, 4)
         res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
-                                       ((t["index_score"] + t["topk"]) * 1e-3) / 1e9, 1)
+                                       ((t["index_score"] + t["topk_page_table"]) * 1e-3) / 1e9, 1)
     if case.prefill:
         res["attn_tflops_kernel_call"] = round(a["attn_flops"] / (t["attn"] * 1e-3) / 1e12, 2)
         res["attn_tflops_with_merge"] = round(a["attn_flops"] /
@@ -311,8 +311,8 @@ def main():
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4),
-        launch=("eager five-call step" if args.eager_only else
-                "hip graph replay of the five-call step (eager ms_per_step also reported)"),
+        launch=("eager four-call step" if args.eager_only else
+                "hip graph replay of the four-call step (eager ms_per_step also reported)"),
         eager_ms_per_step=round(main_run["eager_ms_per_step"], 4), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=main_case.name, batch=main_case.rows,

@@ -7,7 +7,7 @@ codes into exceptions.  There is no CPU fallback: when ``libmsa.so`` is missing
 the first call raises.
 
 Calls (same names and meaning as the C functions):
-    msa_index_score, msa_topk_blocks, msa_build_page_table,
+    msa_index_score, msa_topk_blocks, msa_build_page_table, msa_topk_blocks_paged,
     msa_sparse_attn_decode, msa_prefill_workspace_size, msa_sparse_attn_prefill,
     msa_lse_merge, msa_version
 """
@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     msa_sparse_attn_decode,
     msa_sparse_attn_prefill,
     msa_topk_blocks,
+    msa_topk_blocks_paged,
     msa_version,
     view_of,
 )

@@ -45,6 +45,7 @@ _DIMS = ctypes.POINTER(Dims)
 _SIGS = {
     "msa_index_score": [_DIMS, _I32, _P, View, _P, _I32, _P, _P, _P, _I32, _P, _I32, _P],
     "msa_topk_blocks": [_DIMS, _I32, _P, _I32, _P, _I32, _P, _P],
+    "msa_topk_blocks_paged": [_DIMS, _I32, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P],
     "msa_build_page_table": [_DIMS, _I32, _P, _I32, _P, _P, _I32, _P, _P],
     "msa_sparse_attn_decode": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, ctypes.c_float,
                                _P, _P, _P],
@@ -158,6 +159,24 @@ def msa_topk_blocks(dims: Dims, scores, row_pos, k, sel=None, stream=None):
                                   _ptr(row_pos), k, _ptr(sel), _stream(stream)),
            "msa_topk_blocks")
     return sel
+
+
+def msa_topk_blocks_paged(dims: Dims, scores, row_pos, k, block_table, row_req=None, sel=None,
+                          page_table=None, stream=None):
+    """msa_topk_blocks and msa_build_page_table in one launch; returns (sel, page_table)."""
+    _need(scores, torch.float32, "scores", True)
+    _i32(row_pos, "row_pos"), _i32(block_table, "block_table"), _i32(row_req, "row_req")
+    rows, _, score_stride = scores.shape
+    if sel is None:
+        sel = torch.empty((rows, dims.G, k + 1), dtype=torch.int32, device=scores.device)
+    if page_table is None:
+        page_table = torch.empty_like(sel)
+    _check(load().msa_topk_blocks_paged(ctypes.byref(dims), rows, _ptr(scores), score_stride,
+                                        _ptr(row_pos), k, _ptr(row_req), _ptr(block_table),
+                                        block_table.shape[1], _ptr(sel), _ptr(page_table),
+                                        _stream(stream)),
+           "msa_topk_blocks_paged")
+    return sel, page_table
 
 
 def msa_build_page_table(dims: Dims, sel, block_table, row_req=None, page_table=None,

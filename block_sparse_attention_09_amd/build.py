@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.cpp", "index_score.hip", "topk.hip", "attn.hip", "merge.hip"]
+SOURCES = ["msa_api.cpp", "index_score.hip", "index_score_tiled.hip", "topk.hip", "attn.hip",
+           "merge.hip"]
 ARCH = "gfx950"
 
 

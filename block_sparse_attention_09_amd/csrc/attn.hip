@@ -431,7 +431,8 @@ __device__ __forceinline__ v4i16 lds_read_tr(const char *lds_byte_addr) {
 }
 
 template <int HG>
-__global__ __launch_bounds__(kDecThreads, 5) void attn_decode_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void attn_decode_kernel(
+    AttnArgs a, float scale_log2) {
     __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
     using C = DecComb<HG>;
     // maxima and sums of wave i: ml(i)[0 .. 15] and ml(i)[16 .. 31]

@@ -133,6 +133,26 @@ msa_status_t msa_topk_blocks(const msa_dims_t *dims, int32_t rows, const float *
                       "msa_topk_blocks");
 }
 
+msa_status_t msa_topk_blocks_paged(const msa_dims_t *dims, int32_t rows, const float *scores,
+                                   int32_t score_stride, const int32_t *row_pos, int32_t k,
+                                   const int32_t *row_req, const int32_t *block_table,
+                                   int32_t bt_stride, int32_t *sel, int32_t *page_table,
+                                   msa_stream_t stream) {
+    msa_status_t st = check_dims(dims, false, false);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    REQUIRE(k >= 0, MSA_ERR_INVALID, "k = %d must be >= 0", k);
+    REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
+    REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
+    if (rows == 0) return ok();
+    REQUIRE(scores && row_pos && sel && block_table && page_table, MSA_ERR_NULL,
+            "scores, row_pos, block_table, sel and page_table are required");
+    return hip_status(msa::launch_topk(rows, dims->G, scores, score_stride, row_pos, k, sel,
+                                       as_stream(stream), row_req, block_table, bt_stride,
+                                       page_table),
+                      "msa_topk_blocks_paged");
+}
+
 msa_status_t msa_build_page_table(const msa_dims_t *dims, int32_t rows, const int32_t *sel,
                                   int32_t nslot, const int32_t *row_req,
                                   const int32_t *block_table, int32_t bt_stride,

@@ -69,8 +69,19 @@ hipError_t launch_index_score(const msa_dims_t &d, int rows, const bf16_t *q_idx
                               const int32_t *blk_lo, int num_reqs, float *scores,
                               int score_stride, hipStream_t stream);
 
+// With page_table != nullptr the page of every selected block is written too
+// (block_table[row_req[r]][sel], -1 for empty slots).
+// Prefill shape (many rows per request): the row-tiled scorer.
+hipError_t launch_index_score_tiled(const msa_dims_t &d, int rows, const bf16_t *q_idx,
+                                    const msa_view_t &kv, const int32_t *block_table,
+                                    int bt_stride, const int32_t *row_req, const int32_t *row_pos,
+                                    const int32_t *blk_lo, float *scores, int score_stride,
+                                    hipStream_t stream);
+
 hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
-                       const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream);
+                       const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream,
+                       const int32_t *row_req = nullptr, const int32_t *block_table = nullptr,
+                       int bt_stride = 0, int32_t *page_table = nullptr);
 
 hipError_t launch_page_table(int rows, int G, const int32_t *sel, int nslot,
                              const int32_t *row_req, const int32_t *block_table, int bt_stride,

@@ -33,6 +33,33 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 // Exclusive prefix count of `flag` over the workgroup in thread order; returns
 // the prefix for this thread and writes the workgroup total to *total.
+// Optional page-table output written next to the selection: page of slot i =
+// block_table[request][sel[i]], -1 for an empty slot.  With pt == nullptr the
+// top-k kernels write the selection only.
+struct PageRow {
+    const int32_t *bt;  // this row's block-table row
+    int32_t *pt;        // this (row, group)'s page-table slots, or nullptr
+    __device__ __forceinline__ void put(int i, int b) const {
+        if (pt) pt[i] = (b < 0) ? -1 : bt[b];
+    }
+};
+struct PageOut {
+    const int32_t *block_table;
+    int bt_stride;
+    const int32_t *row_req;
+    int32_t *pt;
+    __device__ __forceinline__ PageRow row(int rg, int G, int k) const {
+        PageRow pr{nullptr, nullptr};
+        if (pt) {
+            const int r = rg / G;
+            const int req = row_req ? row_req[r] : r;
+            pr.bt = block_table + (int64_t)req * bt_stride;
+            pr.pt = pt + (int64_t)rg * (k + 1);
+        }
+        return pr;
+    }
+};
+
 template <int NWAVES = kTopkWaves>
 __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int *total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -92,7 +119,8 @@ template <int THREADS, int KPT>
 __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *__restrict__ scores,
                                                            int score_stride,
                                                            const int32_t *__restrict__ row_pos,
-                                                           int k, int32_t *__restrict__ sel) {
+                                                           int k, int32_t *__restrict__ sel,
+                                                           PageOut po) {
     constexpr int NW = THREADS / kWave;
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[NW];
@@ -102,6 +130,7 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
     const int own = row_pos[rg / G] / kBlk;
     const float *s = scores + (int64_t)rg * score_stride;
     int32_t *out = sel + (int64_t)rg * (k + 1);
+    const PageRow pr = po.row(rg, G, k);
 
     // key 0 marks "not a candidate"; every finite score's key is > 0
     uint32_t key[KPT];
@@ -169,17 +198,25 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
         const bool keep = valid && (key[i] > thresh || (is_eq && eq_rank < take_eq));
         int keep_tot;
         const int at = n_sel + block_excl_count<NW>(keep, wave_tot, &keep_tot);
-        if (keep) out[at] = b;
+        if (keep) {
+            out[at] = b;
+            pr.put(at, b);
+        }
         n_sel += keep_tot;
         n_eq += eq_tot;
     }
-    for (int i = n_sel + tid; i <= k; i += THREADS) out[i] = (i == n_sel) ? own : -1;
+    for (int i = n_sel + tid; i <= k; i += THREADS) {
+        const int b = (i == n_sel) ? own : -1;
+        out[i] = b;
+        pr.put(i, b);
+    }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *__restrict__ scores,
                                                            int score_stride,
                                                            const int32_t *__restrict__ row_pos,
-                                                           int k, int32_t *__restrict__ sel) {
+                                                           int k, int32_t *__restrict__ sel,
+                                                           PageOut po) {
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[kTopkWaves];
     __shared__ int sh_digit, sh_above;
@@ -190,6 +227,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
     const int own = row_pos[r] / kBlk;
     const float *s = scores + (int64_t)rg * score_stride;
     int32_t *out = sel + (int64_t)rg * (k + 1);
+    const PageRow pr = po.row(rg, G, k);
 
     // number of candidates: blocks before own with a score other than -inf
     int ncand = 0;
@@ -245,11 +283,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
         const bool keep = valid && (key > thresh || (is_eq && eq_rank < take_eq));
         int keep_tot;
         const int at = n_sel + block_excl_count(keep, wave_tot, &keep_tot);
-        if (keep) out[at] = b;
+        if (keep) {
+            out[at] = b;
+            pr.put(at, b);
+        }
         n_sel += keep_tot;
         n_eq += eq_tot;
     }
-    for (int i = n_sel + tid; i <= k; i += kTopkThreads) out[i] = (i == n_sel) ? own : -1;
+    for (int i = n_sel + tid; i <= k; i += kTopkThreads) {
+        const int b = (i == n_sel) ? own : -1;
+        out[i] = b;
+        pr.put(i, b);
+    }
 }
 
 __global__ void page_table_kernel(int64_t n, int G, int nslot, const int32_t *__restrict__ sel,
@@ -267,20 +312,23 @@ __global__ void page_table_kernel(int64_t n, int G, int nslot, const int32_t *__
 }  // namespace
 
 hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
-                       const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream) {
+                       const int32_t *row_pos, int k, int32_t *sel, hipStream_t stream,
+                       const int32_t *row_req, const int32_t *block_table, int bt_stride,
+                       int32_t *page_table) {
     const dim3 grid((unsigned)((int64_t)rows * G));
+    const PageOut po{block_table, bt_stride, row_req, page_table};
     // scores per (row, group) held in registers: one wave up to 1024 blocks,
     // a 256-thread workgroup up to 16384; beyond that the global-memory kernel
 #define MSA_TOPK_REG(T, K)                                                                  \
     hipLaunchKernelGGL((topk_reg_kernel<T, K>), grid, dim3(T), 0, stream, G, scores,        \
-                       score_stride, row_pos, k, sel)
+                       score_stride, row_pos, k, sel, po)
     if (score_stride <= 64 * 8) MSA_TOPK_REG(64, 8);
     else if (score_stride <= 64 * 16) MSA_TOPK_REG(64, 16);
     else if (score_stride <= 256 * 16) MSA_TOPK_REG(256, 16);
     else if (score_stride <= 256 * 32) MSA_TOPK_REG(256, 32);
     else if (score_stride <= 256 * 64) MSA_TOPK_REG(256, 64);
     else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, stream, G, scores,
-                            score_stride, row_pos, k, sel);
+                            score_stride, row_pos, k, sel, po);
 #undef MSA_TOPK_REG
     return hipGetLastError();
 }

@@ -144,6 +144,21 @@ msa_status_t msa_build_page_table(const msa_dims_t *dims, int32_t rows, const in
                                   const int32_t *block_table, int32_t bt_stride,
                                   int32_t *page_table, msa_stream_t stream);
 
+/* ------------------------------------------------------------------ a2 + a3
+ * msa_topk_blocks_paged -- msa_topk_blocks and msa_build_page_table in one
+ * kernel.  Pages: the new smaller kernels of the path (the top-k among them)
+ * are named as fusion candidates (未来工作); the page table is the lookup of
+ * 将 MSA 与分页注意力集成.
+ *
+ * Writes exactly what msa_topk_blocks (sel, nslot = k + 1) followed by
+ * msa_build_page_table (page_table) write, bit for bit, with one launch and
+ * without reading sel back.  Arguments as in those two calls. */
+msa_status_t msa_topk_blocks_paged(const msa_dims_t *dims, int32_t rows, const float *scores,
+                                   int32_t score_stride, const int32_t *row_pos, int32_t k,
+                                   const int32_t *row_req, const int32_t *block_table,
+                                   int32_t bt_stride, int32_t *sel, int32_t *page_table,
+                                   msa_stream_t stream);
+
 /* ------------------------------------------------------------------ a4
  * msa_sparse_attn_decode -- per-block partial attention for decode rows.
  * Pages: dense attention over the selected blocks (架构/特性), read through the

@@ -41,6 +41,11 @@ def gpu_path(case, prefill=None, sel=None, pt=None, sm_scale=None):
                                  num_reqs=case.num_reqs)
     sel_gpu = msa.msa_topk_blocks(d, scores, case.row_pos, case.k)
     pt_gpu = msa.msa_build_page_table(d, sel_gpu, case.block_table, row_req=case.row_req)
+    # the fused selection + page-table call writes the same two arrays, bit for bit
+    sel_f, pt_f = msa.msa_topk_blocks_paged(d, scores, case.row_pos, case.k, case.block_table,
+                                            row_req=case.row_req)
+    assert torch.equal(sel_f, sel_gpu), "msa_topk_blocks_paged: sel differs"
+    assert torch.equal(pt_f, pt_gpu), "msa_topk_blocks_paged: page table differs"
     use_sel = sel_gpu if sel is None else sel
     use_pt = pt_gpu if pt is None else pt
     if prefill is None:

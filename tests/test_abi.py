@@ -99,6 +99,17 @@ def test_topk_and_page_table_validation(lib):
                                     None) == MSA_ERR_INVALID
     assert lib.msa_build_page_table(ctypes.byref(d), 1, None, 3, None, FAKE, 4, FAKE,
                                     None) == MSA_ERR_NULL
+    paged = lib.msa_topk_blocks_paged
+    assert paged(ctypes.byref(d), 1, FAKE, 4, FAKE, -1, None, FAKE, 4, FAKE, FAKE,
+                 None) == MSA_ERR_INVALID
+    assert paged(ctypes.byref(d), 1, FAKE, 4, FAKE, 2, None, FAKE, 0, FAKE, FAKE,
+                 None) == MSA_ERR_INVALID
+    assert paged(ctypes.byref(d), 1, FAKE, 4, FAKE, 2, None, None, 4, FAKE, FAKE,
+                 None) == MSA_ERR_NULL
+    assert paged(ctypes.byref(d), 1, FAKE, 4, FAKE, 2, None, FAKE, 4, FAKE, None,
+                 None) == MSA_ERR_NULL
+    assert paged(ctypes.byref(d), 0, None, 4, None, 2, None, None, 4, None, None,
+                 None) == MSA_OK
 
 
 def _decode(lib, dims, **kw):

@@ -95,11 +95,18 @@ def test_topk_exact_on_oracle_scores(nb):
     pos[0], pos[2] = 5, 130
     pos[3] = nb * 128 - 1
     d = msa.Dims(G=G, Hg=1, D=128, n_idx=4, d_idx=128, blk=128)
+    # a random block table (one request per row) for the fused page-table output
+    bt = rng.integers(0, 1 << 20, size=(rows, nb)).astype(np.int32)
+    sc_d, pos_d, bt_d = (torch.tensor(x, device=DEV) for x in (sc, pos, bt))
     for k in (0, 1, 7, 16, 33, 300, nb + 5):
         want = oracle.topk(sc, pos, k)
-        got = msa.msa_topk_blocks(d, torch.tensor(sc, device=DEV),
-                                  torch.tensor(pos, device=DEV), k).cpu().numpy()
+        got = msa.msa_topk_blocks(d, sc_d, pos_d, k).cpu().numpy()
         assert np.array_equal(got, want), f"k={k}"
+        sel_f, pt_f = msa.msa_topk_blocks_paged(d, sc_d, pos_d, k, bt_d)
+        assert np.array_equal(sel_f.cpu().numpy(), want), f"paged k={k}"
+        assert np.array_equal(pt_f.cpu().numpy(),
+                              oracle.page_table(want, bt, np.arange(rows, dtype=np.int32))), \
+            f"paged page table k={k}"
 
 
 def test_prefill_and_decode_agree_with_oracle():
