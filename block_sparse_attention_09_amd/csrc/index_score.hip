@@ -32,10 +32,6 @@ namespace msa {
 
 namespace {
 
-#ifndef MSA_SCORE_NT
-#define MSA_SCORE_NT 1
-#endif
-
 constexpr int kTilesPerStep = 4;   // 4 x 16 tokens = half a block per register buffer
 constexpr int kMaxChunk = 64;      // chunk length bound: one page id per lane
 
@@ -46,11 +42,7 @@ struct StepBuf {
 
 // Key-index stream: read once, never reused -> non-temporal loads.
 __device__ __forceinline__ u32x4 ld16_stream(const bf16_t *p) {
-#if MSA_SCORE_NT
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-#else
-    return ld16(p);
-#endif
 }
 
 template <int DIDX>
