@@ -28,6 +28,8 @@
 // inversion of the selection built in the caller's workspace.
 #include "msa_internal.h"
 
+#include <algorithm>
+
 namespace msa {
 
 namespace {
@@ -285,7 +287,8 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, const AttnAr
 }
 
 // ------------------------------------------------------------------ prefill
-// Workspace: counts[G*P] | offs[G*P + 1] | list[rows*G*nslot] (int32 each).
+// Workspace: cnt[G*P][W] | counts[G*P] | offs[G*P + 1] | list[rows*G*nslot]
+// (int32 each; W = workgroups of the counting sort, cnt unused when W = 0).
 // Units are numbered u = page * G + g, so that with the default round-robin
 // dispatch over the 8 XCDs the units of one KV group (and its query rows) stay
 // on one XCD's L2 when G is 8.
@@ -353,6 +356,87 @@ __global__ void remap_scatter_kernel(AttnArgs a, int32_t *__restrict__ cursor,
     const int64_t u = (int64_t)a.page_table[i] * a.G + g;
     const int at = atomicAdd(&cursor[u], 1);
     list[offs[u] + at] = r * a.nslot + s;
+}
+
+// Multi-workgroup counting sort (used while the G * P units fit an LDS
+// histogram): workgroup w takes a contiguous chunk of the flattened (row,
+// group, slot) selection, counts it per unit in LDS and writes its counts to
+// column w of cnt[unit][W]; a wave per unit turns each row of cnt into an
+// exclusive prefix over the workgroups (and the unit's total), the
+// single-workgroup scan turns the totals into list offsets, and each workgroup
+// places its chunk again with LDS cursors.  No global atomics: the atomic
+// inversion costs two contended global atomics per entry.
+constexpr int kRemapThreads = 1024;
+constexpr int kRemapMaxUnits = 16384;  // LDS histogram of 64 KB
+
+__device__ __forceinline__ void remap_entry(const AttnArgs &a, int64_t i, int &r, int &g, int &s) {
+    s = (int)(i % a.nslot);
+    const int rg = (int)(i / a.nslot);
+    g = rg % a.G;
+    r = rg / a.G;
+}
+
+template <int HG>
+__global__ __launch_bounds__(kRemapThreads) void remap_hist_kernel(AttnArgs a, int units, int W,
+                                                                   int64_t chunk,
+                                                                   int32_t *__restrict__ cnt) {
+    __shared__ int32_t hist[kRemapMaxUnits];
+    for (int u = threadIdx.x; u < units; u += kRemapThreads) hist[u] = 0;
+    __syncthreads();
+    const int w = blockIdx.x;
+    const int64_t n = (int64_t)a.rows * a.G * a.nslot;
+    const int64_t i1 = min(n, (w + 1) * chunk);
+    for (int64_t i = w * chunk + threadIdx.x; i < i1; i += kRemapThreads) {
+        int r, g, s;
+        remap_entry(a, i, r, g, s);
+        if (a.sel[i] < 0) {
+            write_empty_slot<HG>(a, r, g, s, 0, 1);
+            continue;
+        }
+        atomicAdd(&hist[a.page_table[i] * a.G + g], 1);
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < units; u += kRemapThreads) cnt[(int64_t)u * W + w] = hist[u];
+}
+
+__global__ void remap_unitscan_kernel(int units, int W, int32_t *__restrict__ cnt,
+                                      int32_t *__restrict__ total) {
+    const int lane = threadIdx.x & 63;
+    const int u = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+    if (u >= units) return;  // whole waves leave together
+    int32_t *c = cnt + (int64_t)u * W;
+    int run = 0;
+    for (int w0 = 0; w0 < W; w0 += kWave) {
+        const int x = (w0 + lane < W) ? c[w0 + lane] : 0;
+        int incl = x;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(incl, off, kWave);
+            incl += (lane >= off) ? v : 0;
+        }
+        if (w0 + lane < W) c[w0 + lane] = run + incl - x;
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) total[u] = run;
+}
+
+__global__ __launch_bounds__(kRemapThreads) void remap_place_kernel(
+    AttnArgs a, int units, int W, int64_t chunk, const int32_t *__restrict__ cnt,
+    const int32_t *__restrict__ offs, int32_t *__restrict__ list) {
+    __shared__ int32_t cur[kRemapMaxUnits];
+    for (int u = threadIdx.x; u < units; u += kRemapThreads) cur[u] = 0;
+    __syncthreads();
+    const int w = blockIdx.x;
+    const int64_t n = (int64_t)a.rows * a.G * a.nslot;
+    const int64_t i1 = min(n, (w + 1) * chunk);
+    for (int64_t i = w * chunk + threadIdx.x; i < i1; i += kRemapThreads) {
+        if (a.sel[i] < 0) continue;
+        int r, g, s;
+        remap_entry(a, i, r, g, s);
+        const int u = a.page_table[i] * a.G + g;
+        const int at = atomicAdd(&cur[u], 1);
+        list[offs[u] + cnt[(int64_t)u * W + w] + at] = r * a.nslot + s;
+    }
 }
 
 template <int HG>
@@ -615,33 +699,64 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workgroups of the counting sort: enough that each chunk is a few times the
+// unit count, at most 256; 0 selects the atomic inversion (units beyond the
+// LDS histogram).
+static int remap_workgroups(int64_t n, int64_t units) {
+    if (units > kRemapMaxUnits) return 0;
+    const int64_t w = n / (4 * units + 1) + 1;
+    return (int)std::min<int64_t>(256, w);
+}
+
 size_t prefill_workspace_bytes(int rows, int G, int nslot, int num_pages) {
     const size_t units = (size_t)G * num_pages;
-    return align256(units * 4) + align256((units + 1) * 4) + align256((size_t)rows * G * nslot * 4);
+    const int64_t n = (int64_t)rows * G * nslot;
+    const int W = remap_workgroups(n, (int64_t)units);
+    return align256(units * (size_t)std::max(W, 1) * 4) + align256(units * 4) +
+           align256((units + 1) * 4) + align256((size_t)n * 4);
 }
 
 hipError_t launch_attn_prefill(const AttnArgs &a, int P, void *workspace, hipStream_t stream) {
     const int64_t units = (int64_t)a.G * P;
-    char *ws = static_cast<char *>(workspace);
-    int32_t *counts = reinterpret_cast<int32_t *>(ws);
-    int32_t *offs = reinterpret_cast<int32_t *>(ws + align256(units * 4));
-    int32_t *list = reinterpret_cast<int32_t *>(ws + align256(units * 4) + align256((units + 1) * 4));
     const int64_t n = (int64_t)a.rows * a.G * a.nslot;
+    const int W = remap_workgroups(n, units);
+    char *ws = static_cast<char *>(workspace);
+    int32_t *cnt = reinterpret_cast<int32_t *>(ws);
+    ws += align256((size_t)units * std::max(W, 1) * 4);
+    int32_t *counts = reinterpret_cast<int32_t *>(ws);
+    ws += align256((size_t)units * 4);
+    int32_t *offs = reinterpret_cast<int32_t *>(ws);
+    ws += align256((size_t)(units + 1) * 4);
+    int32_t *list = reinterpret_cast<int32_t *>(ws);
     const float sl2 = a.sm_scale * kLog2e;
 
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
-                       counts, units, 0);
-    const dim3 eg((unsigned)((n + 255) / 256)), eb(256);
-    switch (a.Hg) {
-        case 1: hipLaunchKernelGGL(remap_count_kernel<1>, eg, eb, 0, stream, a, counts); break;
-        case 2: hipLaunchKernelGGL(remap_count_kernel<2>, eg, eb, 0, stream, a, counts); break;
-        case 4: hipLaunchKernelGGL(remap_count_kernel<4>, eg, eb, 0, stream, a, counts); break;
-        case 8: hipLaunchKernelGGL(remap_count_kernel<8>, eg, eb, 0, stream, a, counts); break;
-        default: hipLaunchKernelGGL(remap_count_kernel<16>, eg, eb, 0, stream, a, counts); break;
+#define MSA_BY_HG(KERNEL, GRID, BLOCK, ...)                                                      \
+    switch (a.Hg) {                                                                              \
+        case 1: hipLaunchKernelGGL(KERNEL<1>, GRID, BLOCK, 0, stream, __VA_ARGS__); break;       \
+        case 2: hipLaunchKernelGGL(KERNEL<2>, GRID, BLOCK, 0, stream, __VA_ARGS__); break;       \
+        case 4: hipLaunchKernelGGL(KERNEL<4>, GRID, BLOCK, 0, stream, __VA_ARGS__); break;       \
+        case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, BLOCK, 0, stream, __VA_ARGS__); break;       \
+        default: hipLaunchKernelGGL(KERNEL<16>, GRID, BLOCK, 0, stream, __VA_ARGS__); break;     \
     }
-    hipLaunchKernelGGL(remap_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, offs,
-                       (int)units);
-    hipLaunchKernelGGL(remap_scatter_kernel, eg, eb, 0, stream, a, counts, offs, list);
+    if (W > 0) {
+        const int64_t chunk = (n + W - 1) / W;
+        MSA_BY_HG(remap_hist_kernel, dim3(W), dim3(kRemapThreads), a, (int)units, W, chunk, cnt)
+        hipLaunchKernelGGL(remap_unitscan_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0,
+                           stream, (int)units, W, cnt, counts);
+        hipLaunchKernelGGL(remap_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts,
+                           offs, (int)units);
+        hipLaunchKernelGGL(remap_place_kernel, dim3(W), dim3(kRemapThreads), 0, stream, a,
+                           (int)units, W, chunk, cnt, offs, list);
+    } else {
+        hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
+                           stream, counts, units, 0);
+        const dim3 eg((unsigned)((n + 255) / 256)), eb(256);
+        MSA_BY_HG(remap_count_kernel, eg, eb, a, counts)
+        hipLaunchKernelGGL(remap_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts,
+                           offs, (int)units);
+        hipLaunchKernelGGL(remap_scatter_kernel, eg, eb, 0, stream, a, counts, offs, list);
+    }
+#undef MSA_BY_HG
     const dim3 grid((unsigned)units), block(kAttnThreads);
     switch (a.Hg) {
         case 1: hipLaunchKernelGGL(attn_blockmajor_kernel<1>, grid, block, 0, stream, a, offs, list, sl2); break;

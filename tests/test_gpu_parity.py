@@ -167,6 +167,10 @@ PREFILL_SHAPES = {
     # only the own block, and every earlier block
     "k0": dict(seed=208, ctx_lens=[1000], G=2, Hg=8, d_idx=64, k=0, prefill_rows=200),
     "k-all": dict(seed=209, ctx_lens=[1000], G=2, Hg=8, d_idx=64, k=50, prefill_rows=200),
+    # 4 groups x 4,200 pages = 16,800 (group, page) units: more than the LDS
+    # histogram of the counting sort holds, so the atomic inversion runs
+    "big-pool": dict(seed=210, ctx_lens=[1500], G=4, Hg=2, d_idx=64, k=3, prefill_rows=150,
+                     pool_pages=4200),
 }
 
 
