@@ -137,9 +137,12 @@ def test_prefill_workspace(lib):
     n = ctypes.c_size_t(0)
     assert lib.msa_prefill_workspace_size(ctypes.byref(d), 8192, 17, 544, ctypes.byref(n)) == MSA_OK
     need = n.value
-    # counts + offsets per (group, page) and one entry per (row, group, slot)
-    assert need >= 4 * (2 * 8 * 544 + 1 + 8192 * 8 * 17)
-    assert need < 4 * (2 * 8 * 544 + 1 + 8192 * 8 * 17) + 1024
+    units, entries = 8 * 544, 8192 * 8 * 17
+    # at least counts + offsets per (group, page) unit and one list entry per
+    # (row, group, slot); at most that plus the counting sort's per-workgroup
+    # counts (<= 256 workgroups) and alignment padding
+    assert need >= 4 * (2 * units + 1 + entries)
+    assert need <= 4 * (258 * units + 1 + entries) + 1024
     st = lib.msa_sparse_attn_prefill(ctypes.byref(d), 8192, FAKE, _view(), _view(), FAKE, FAKE,
                                      17, FAKE, 544, 0.088, FAKE, need - 1, FAKE, FAKE, None)
     assert st == MSA_ERR_WORKSPACE
