@@ -4,9 +4,10 @@
 
 A step is one pass of the whole path over one batch: index scores, top-k with
 the page table (msa_topk_blocks_paged: one kernel writes both), sparse attention
-(decode kernel, or the KV-block-major prefill), LSE merge.  The headline line is the decode workload at 64K context, batch 8
-(8 KV groups x 8 heads, d_idx 128, top-16 + own block, paged):
-value = decode tokens/s of one MSA layer = batch x steps / time.
+(decode kernel, or the KV-block-major prefill), LSE merge.  The headline line is
+the decode workload at 64K context, batch 8 (8 KV groups x 8 heads, d_idx 128,
+top-16 + own block, paged): value = decode tokens/s of one MSA layer
+= batch x steps / time.
 
 Also reported on the same line:
   roofline      the index-score kernel (dominant: >90% of the step's bytes)
@@ -236,6 +237,8 @@ def summarize(cfg, case, r):
         res["index_score_hbm_frac"] = round(score_gbps / HBM_PEAK_GBPS, 4)
         res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
                                        ((t["index_score"] + t["topk_page_table"]) * 1e-3) / 1e9, 1)
+    merge_bytes = a["part_bytes"] + a["qo_bytes"] // 2   # partials read, output written
+    res["merge_GBps"] = round(merge_bytes / (t["merge"] * 1e-3) / 1e9, 1)
     if case.prefill:
         res["attn_tflops_kernel_call"] = round(a["attn_flops"] / (t["attn"] * 1e-3) / 1e12, 2)
         res["attn_tflops_with_merge"] = round(a["attn_flops"] /
@@ -254,6 +257,7 @@ def summarize(cfg, case, r):
         res["step_alg_GBps"] = round(step_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1)
         attn_bytes = a["kv_bytes"] + a["qo_bytes"] // 2 + a["part_bytes"]
         res["decode_attn_GBps"] = round(attn_bytes / (t["attn"] * 1e-3) / 1e9, 1)
+        res["decode_attn_hbm_frac"] = round(res["decode_attn_GBps"] / HBM_PEAK_GBPS, 4)
     return res
 
 

@@ -12,20 +12,23 @@
 //    HBM once, and each block yields partial outputs that a final log-sum-exp
 //    reduction rescales and sums.
 //
-// One workgroup serves one (KV group, page) unit: it stages K (row-major) and V
-// (transposed) in LDS once, then its four waves take tiles of 32 query rows
-// (32 / Hg query tokens x Hg heads) against the whole 128-token block on the
-// 32x32x16 bf16 matrix cores:
+// Prefill: one workgroup serves one (KV group, page) unit: it stages K
+// (row-major) and V (transposed) in LDS once, then its four waves take tiles of
+// 32 query rows (32 / Hg query tokens x Hg heads) against the whole 128-token
+// block on the 32x32x16 bf16 matrix cores:
 //   S^T = K Q^T    K from LDS (A), Q straight from global (B)
 //   softmax        per query row over the block's causally visible tokens,
 //                  exp2 with log2(e) folded into the scale, fp32 row sums
 //   O^T = V^T P^T  V^T from LDS in the token order that matches where the S^T
 //                  accumulators leave P, P^T repacked to bf16 in registers
 // and writes the normalised partial (bf16) and its natural-log LSE (fp32).
-// A wave needs about 200 registers, so two workgroups (eight waves) share a CU
-// and one wave's softmax overlaps another's matrix-core work.
-// Decode units hold one query row each; prefill units come from a counting-sort
-// inversion of the selection built in the caller's workspace.
+// A wave needs about 250 registers, so two workgroups (eight waves) share a CU
+// and one wave's softmax overlaps another's matrix-core work.  The units' query
+// lists come from a counting-sort inversion of the selection built in the
+// caller's workspace.
+//
+// Decode: one workgroup per (row, group, slot), the block split over its four
+// waves (see attn_decode_kernel below).
 #include "msa_internal.h"
 
 #include <algorithm>
