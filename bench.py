@@ -145,12 +145,15 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
     eager_ms = t0.elapsed_time(t1)
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
            for j, n in enumerate(names)}
+    # spread of the eager step (first call start to last call end, per step)
+    step_ms = sorted(evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(steps))
+    pct = {q: step_ms[min(steps - 1, int(round(q / 100 * (steps - 1))))] for q in (10, 50, 90)}
     o_ref, lse_ref = o.clone(), lse.clone()
     alg = algorithmic(case, sel)
     if not graph_replay:
         return case, dict(total_ms=eager_ms, ms_per_step=eager_ms / steps, eager_ms=eager_ms,
                           eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
-                          alg=alg, sel=sel.cpu())
+                          step_pct_ms=pct, alg=alg, sel=sel.cpu())
 
     # The same step captured once in a HIP graph and replayed: removes the
     # host launch gaps between the calls.  Every replay must reproduce the
@@ -181,8 +184,8 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
     if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref)):
         raise RuntimeError(f"{case.name}: graph replay differs from the eager step")
     return case, dict(total_ms=graph_ms, ms_per_step=graph_ms / steps, eager_ms=eager_ms,
-                      eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per, alg=alg,
-                      sel=sel.cpu())
+                      eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
+                      step_pct_ms=pct, alg=alg, sel=sel.cpu())
 
 
 def traffic_from_profile():
@@ -230,6 +233,7 @@ def summarize(cfg, case, r):
     t = r["per_call_ms"]
     res = dict(workload=case.name, ms_per_step=round(r["ms_per_step"], 4),
                eager_ms_per_step=round(r["eager_ms_per_step"], 4),
+               eager_step_ms_p10_p50_p90=[round(r["step_pct_ms"][q], 4) for q in (10, 50, 90)],
                per_call_us={k: round(v * 1e3, 2) for k, v in t.items()})
     if not case.prefill:
         score_gbps = a["score_bytes"] / (t["index_score"] * 1e-3) / 1e9

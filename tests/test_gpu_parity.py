@@ -201,6 +201,25 @@ def test_prefill_several_requests():
     pu.check_output(res["o"], res["lse"], o, lse)
 
 
+def test_side_stream_matches_default_stream():
+    """Every call runs on the caller's stream: the whole path (decode and
+    prefill) issued on a side stream gives the default stream's results."""
+    print("[case] side stream", flush=True)
+    for prefill in (False, True):
+        kw = dict(seed=302, ctx_lens=[2100, 900], G=2, Hg=4, d_idx=64, k=3, paged=True)
+        if prefill:
+            kw["prefill_rows"] = [120, 70]
+        case = _build(**kw)
+        a = pu.gpu_path(case)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            b = pu.gpu_path(case)
+        torch.cuda.synchronize()
+        for key in a:
+            assert torch.equal(a[key], b[key]), (prefill, key)
+
+
 def test_deterministic_and_placement_invariant():
     """Two runs are bit-identical; moving pages in the pool (paged vs contiguous)
     and a token-major cache layout give bit-identical results."""
