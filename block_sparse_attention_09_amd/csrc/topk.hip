@@ -8,11 +8,14 @@
 // (将 MSA 与分页注意力集成).
 //
 // Selection = radix select on order-preserving 32-bit keys of the fp32 scores,
-// one workgroup per (row, group): four 8-bit digit passes (LDS histogram, one
-// wave scans it) find the k-th largest key T and how many keys equal to T are
-// still needed; one ordered pass then keeps keys > T plus the lowest-index keys
-// == T (ties go to the lower block index) and compacts them in ascending block
-// order with wave ballots.  The own block is appended last (it is the largest
+// one workgroup per (row, group): 8-bit digit passes (LDS histogram, one wave
+// scans it) find the k-th largest key T and how many keys equal to T are still
+// needed.  The passes start at the highest bit where the candidates' keys
+// differ and stop as soon as the bucket holding T is taken whole, so a few
+// hundred spread scores usually need two passes, not four.  One ordered pass
+// then keeps keys above T plus the lowest-index keys equal to it (ties go to
+// the lower block index), compared on the bits the passes fixed, and compacts
+// them in ascending block order with wave ballots.  The own block is appended last (it is the largest
 // index) and the rest is padded with -1.  Integer decisions on the caller's
 // fp32 scores only, so the result is exact and deterministic.
 #include "msa_internal.h"
@@ -83,6 +86,45 @@ __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int *t
     return before + in_wave;
 }
 
+// Workgroup minimum and maximum of the valid (non-zero) keys: *lo = ~0u and
+// *hi = 0 when there are none.  `xch` holds 2 * NWAVES words of LDS.
+template <int NWAVES>
+__device__ __forceinline__ void key_range(uint32_t lo, uint32_t hi, uint32_t *xch,
+                                          uint32_t *lo_out, uint32_t *hi_out) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
+    }
+    if (NWAVES > 1) {
+        const int w = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) {
+            xch[2 * w] = lo;
+            xch[2 * w + 1] = hi;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) {
+            lo = min(lo, xch[2 * i]);
+            hi = max(hi, xch[2 * i + 1]);
+        }
+        __syncthreads();
+    }
+    *lo_out = lo;
+    *hi_out = hi;
+}
+
+// First digit shift of the radix select: the 8 bits that start at the highest
+// bit where the smallest and largest candidate keys differ (the bits above it
+// are common to every candidate and carry no rank information).  -1 when every
+// candidate key is the same.
+__device__ __forceinline__ int first_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t diff = lo ^ hi;
+    if (diff == 0u) return -1;
+    const int top = 31 - __clz((int)diff);
+    return top > 7 ? top - 7 : 0;
+}
+
 // Digit d of the current radix pass such that the keys above it number fewer
 // than `remain` and those at or above it at least `remain`; one wave scans the
 // 256-bin histogram (4 bins per lane, suffix sums from the top digit down).
@@ -124,6 +166,7 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
     constexpr int NW = THREADS / kWave;
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[NW];
+    __shared__ uint32_t range_xch[2 * NW];
     __shared__ int sh_digit, sh_above;
     const int rg = blockIdx.x;
     const int tid = threadIdx.x;
@@ -135,12 +178,15 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
     // key 0 marks "not a candidate"; every finite score's key is > 0
     uint32_t key[KPT];
     int nvalid = 0;
+    uint32_t klo = ~0u, khi = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int b = i * THREADS + tid;
         const float v = (b < own) ? s[b] : -INFINITY;
         key[i] = (v != -INFINITY) ? order_key(v) : 0u;
         nvalid += key[i] != 0u;
+        klo = (key[i] != 0u) ? min(klo, key[i]) : klo;
+        khi = max(khi, key[i]);
     }
     int ncand;
     {
@@ -160,14 +206,20 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
         }
     }
 
-    uint32_t thresh = 0u;
+    // keep keys whose top bits (tmask) exceed thresh, plus the first take_eq
+    // (in block order) whose top bits equal it
+    uint32_t thresh = 0u, tmask = 0xffffffffu;
     int take_eq = 0;
     if (k == 0) {
         thresh = 0xffffffffu;
     } else if (k < ncand) {
+        uint32_t lo, hi;
+        key_range<NW>(klo, khi, range_xch, &lo, &hi);
         uint32_t prefix = 0u, pmask = 0u;
         int remain = k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
+        // digit passes from the highest differing bit down, 8 bits at a time; the
+        // last one may overlap bits already fixed, which all counted keys share
+        for (int shift = first_shift(lo, hi); shift >= 0; shift = shift > 8 ? shift - 8 : 0) {
             for (int i = tid; i < 256; i += THREADS) hist[i] = 0u;
             __syncthreads();
 #pragma unroll
@@ -180,9 +232,12 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
             prefix |= (uint32_t)sh_digit << shift;
             pmask |= 255u << shift;
             remain -= sh_above;
+            const bool whole_bucket = (int)hist[sh_digit] == remain;
             __syncthreads();
+            if (whole_bucket || shift == 0) break;  // selection decided
         }
         thresh = prefix;
+        tmask = pmask;
         take_eq = remain;
     }
 
@@ -192,10 +247,11 @@ __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *_
         if (i * THREADS >= own) break;  // uniform
         const int b = i * THREADS + tid;
         const bool valid = key[i] != 0u;
-        const bool is_eq = valid && key[i] == thresh && take_eq > 0;
+        const uint32_t kk = key[i] & tmask;
+        const bool is_eq = valid && kk == thresh && take_eq > 0;
         int eq_tot;
         const int eq_rank = n_eq + block_excl_count<NW>(is_eq, wave_tot, &eq_tot);
-        const bool keep = valid && (key[i] > thresh || (is_eq && eq_rank < take_eq));
+        const bool keep = valid && (kk > thresh || (is_eq && eq_rank < take_eq));
         int keep_tot;
         const int at = n_sel + block_excl_count<NW>(keep, wave_tot, &keep_tot);
         if (keep) {
@@ -219,6 +275,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
                                                            PageOut po) {
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[kTopkWaves];
+    __shared__ uint32_t range_xch[2 * kTopkWaves];
     __shared__ int sh_digit, sh_above;
 
     const int rg = blockIdx.x;
@@ -231,21 +288,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
 
     // number of candidates: blocks before own with a score other than -inf
     int ncand = 0;
+    uint32_t klo = ~0u, khi = 0u;
     for (int base = 0; base < own; base += kTopkThreads) {
         const int b = base + tid;
+        const float v = (b < own) ? s[b] : -INFINITY;
+        const bool valid = v != -INFINITY;
+        if (valid) {
+            const uint32_t key = order_key(v);
+            klo = min(klo, key);
+            khi = max(khi, key);
+        }
         int t;
-        block_excl_count(b < own && s[b] != -INFINITY, wave_tot, &t);
+        block_excl_count(valid, wave_tot, &t);
         ncand += t;
     }
 
-    uint32_t thresh = 0u;   // keep keys > thresh ...
-    int take_eq = 0;        // ... plus the first take_eq keys == thresh
+    uint32_t thresh = 0u, tmask = 0xffffffffu;  // keep keys whose top bits (tmask) > thresh ...
+    int take_eq = 0;  // ... plus the first take_eq (in block order) whose top bits == thresh
     if (k == 0) {
         thresh = 0xffffffffu;  // keep nothing but the own block
     } else if (k < ncand) {
+        uint32_t lo, hi;
+        key_range<kTopkWaves>(klo, khi, range_xch, &lo, &hi);
         uint32_t prefix = 0u, pmask = 0u;
         int remain = k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
+        // as in topk_reg_kernel: from the highest differing bit down
+        for (int shift = first_shift(lo, hi); shift >= 0; shift = shift > 8 ? shift - 8 : 0) {
             hist[tid] = 0u;
             __syncthreads();
             for (int b = tid; b < own; b += kTopkThreads) {
@@ -260,9 +328,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
             prefix |= (uint32_t)sh_digit << shift;
             pmask |= 255u << shift;
             remain -= sh_above;
+            const bool whole_bucket = (int)hist[sh_digit] == remain;
             __syncthreads();
+            if (whole_bucket || shift == 0) break;  // selection decided
         }
         thresh = prefix;
+        tmask = pmask;
         take_eq = remain;
     }  // else: every candidate is kept (every finite score's key is > 0)
 
@@ -277,10 +348,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *
             valid = v != -INFINITY;
             key = valid ? order_key(v) : 0u;
         }
-        const bool is_eq = valid && key == thresh && take_eq > 0;
+        const uint32_t kk = key & tmask;
+        const bool is_eq = valid && kk == thresh && take_eq > 0;
         int eq_tot;
         const int eq_rank = n_eq + block_excl_count(is_eq, wave_tot, &eq_tot);
-        const bool keep = valid && (key > thresh || (is_eq && eq_rank < take_eq));
+        const bool keep = valid && (kk > thresh || (is_eq && eq_rank < take_eq));
         int keep_tot;
         const int at = n_sel + block_excl_count(keep, wave_tot, &keep_tot);
         if (keep) {
