@@ -7,7 +7,9 @@ the page table (msa_topk_blocks_paged: one kernel writes both), sparse attention
 (decode kernel, or the KV-block-major prefill), LSE merge.  The headline line is
 the decode workload at 64K context, batch 8 (8 KV groups x 8 heads, d_idx 128,
 top-16 + own block, paged): value = decode tokens/s of one MSA layer
-= batch x steps / time.
+= batch x steps / time.  Each timed step starts from cold caches (an untimed
+1 GiB read runs before it) and is timed by its own HIP event pair;
+the same replays back to back, caches warm, are reported beside it.
 
 Also reported on the same line:
   roofline      the index-score kernel (dominant: >90% of the step's bytes)
@@ -34,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tok/s + index-scan HBM GB/s @64K/1M ctx; prefill sparse-attn TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FLUSH_BYTES = 1 << 30
 MAIN = 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_decode-64k-b8.json")
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc", "index_score.hip")
@@ -80,7 +83,7 @@ def algorithmic(case, sel=None):
     return out
 
 
-def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
+def run_workload(cfg, steps, warmup, graph_replay=True):
     import torch
     import block_sparse_attention_09_amd as msa
     import msa_synth
@@ -127,26 +130,34 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
         msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
         mark(4)
 
+    # Every timed step starts from cold caches: an untimed read of 1 GiB (four
+    # times the 256 MB MALL) runs before it, so a step never finds the previous
+    # step's K/V blocks or partials in L2/MALL (consecutive steps of one layer
+    # would not either: the other layers run in between).  A read leaves the
+    # caches clean, so the step pays no write-back of the flush's own lines.
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_out)
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record()
     for i in range(steps):
-        step(evs[i] if want_events else None)
-    t1.record()
+        flush()
+        step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    eager_ms = t0.elapsed_time(t1)
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
            for j, n in enumerate(names)}
-    # spread of the eager step (first call start to last call end, per step)
+    # the eager step, first call start to last call end, per step
     step_ms = sorted(evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(steps))
+    eager_ms = sum(step_ms)
     pct = {q: step_ms[min(steps - 1, int(round(q / 100 * (steps - 1))))] for q in (10, 50, 90)}
     o_ref, lse_ref = o.clone(), lse.clone()
     alg = algorithmic(case, sel)
@@ -172,20 +183,32 @@ def run_workload(cfg, steps, warmup, want_events=True, graph_replay=True):
     torch.cuda.synchronize()
     if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref)):
         raise RuntimeError(f"{case.name}: graph replay differs from the eager step")
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
+    ge = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     torch.cuda.synchronize()
-    g0.record()
-    for _ in range(steps):
+    for i in range(steps):
+        flush()
+        ge[i][0].record()
         graph.replay()
-    g1.record()
+        ge[i][1].record()
     torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1)
+    graph_ms = sum(b.elapsed_time(e) for b, e in ge)
     if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref)):
         raise RuntimeError(f"{case.name}: graph replay differs from the eager step")
+    # for reference only: the same replays back to back, caches left warm
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0.record()
+    for _ in range(steps):
+        graph.replay()
+    w1.record()
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1)
     return case, dict(total_ms=graph_ms, ms_per_step=graph_ms / steps, eager_ms=eager_ms,
                       eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
-                      step_pct_ms=pct, alg=alg, sel=sel.cpu())
+                      step_pct_ms=pct, alg=alg, sel=sel.cpu(),
+                      warm_ms_per_step=warm_ms / steps)
 
 
 def traffic_from_profile():
@@ -228,17 +251,60 @@ def cpu_baseline(case):
                        "fp64 C oracle")
 
 
-def summarize(cfg, case, r):
+def measured_peaks():
+    """What this device sustains with nothing else in the way (include/msa_peaks.h):
+    a non-temporal streaming read of 4 GiB and a register-resident bf16 MFMA loop.
+    Best of several timed launches after a warm-up."""
+    import torch
+    import block_sparse_attention_09_amd as msa
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+
+    def best(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    t_read = best(lambda: msa.msa_peak_stream_read(buf, sink), 5)
+    del buf
+    torch.cuda.empty_cache()
+    iters = 16384
+    flops = msa.msa_peak_mfma_bf16(iters, sink)
+    t_mfma = best(lambda: msa.msa_peak_mfma_bf16(iters, sink), 3)
+    return dict(stream_read_GBps=round(nbytes / (t_read * 1e-3) / 1e9, 1),
+                mfma_bf16_TFLOPs=round(flops / (t_mfma * 1e-3) / 1e12, 1),
+                method=("msa_peak_stream_read over 4 GiB (a workgroup per 64 KB chunk, 8 "
+                        "non-temporal 16-B loads in flight per thread); msa_peak_mfma_bf16: 4 "
+                        "independent 32x32x16 bf16 MFMA chains per wave, 2 waves per SIMD; best "
+                        "of 5 and 3 launches"))
+
+
+def summarize(cfg, case, r, peaks=None):
     a = r["alg"]
     t = r["per_call_ms"]
     res = dict(workload=case.name, ms_per_step=round(r["ms_per_step"], 4),
                eager_ms_per_step=round(r["eager_ms_per_step"], 4),
                eager_step_ms_p10_p50_p90=[round(r["step_pct_ms"][q], 4) for q in (10, 50, 90)],
                per_call_us={k: round(v * 1e3, 2) for k, v in t.items()})
+    if "warm_ms_per_step" in r:
+        res["warm_cache_ms_per_step"] = round(r["warm_ms_per_step"], 4)
     if not case.prefill:
         score_gbps = a["score_bytes"] / (t["index_score"] * 1e-3) / 1e9
         res["index_score_GBps"] = round(score_gbps, 1)
         res["index_score_hbm_frac"] = round(score_gbps / HBM_PEAK_GBPS, 4)
+        if peaks:
+            res["index_score_frac_of_measured_read"] = round(
+                score_gbps / peaks["stream_read_GBps"], 4)
         res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
                                        ((t["index_score"] + t["topk_page_table"]) * 1e-3) / 1e9, 1)
     merge_bytes = a["part_bytes"] + a["qo_bytes"] // 2   # partials read, output written
@@ -248,6 +314,9 @@ def summarize(cfg, case, r):
         res["attn_tflops_with_merge"] = round(a["attn_flops"] /
                                               ((t["attn"] + t["merge"]) * 1e-3) / 1e12, 2)
         res["attn_mfma_frac_call"] = round(res["attn_tflops_kernel_call"] / BF16_PEAK_TFLOPS, 4)
+        if peaks:
+            res["attn_frac_of_measured_mfma"] = round(
+                res["attn_tflops_kernel_call"] / peaks["mfma_bf16_TFLOPs"], 4)
         res["attn_flops"] = a["attn_flops"]
         # index scoring: the definition's FLOPs (every index vector separately) and
         # the matrix-core FLOPs actually issued (qbar as bf16 hi + lo: 2 passes)
@@ -262,6 +331,9 @@ def summarize(cfg, case, r):
         attn_bytes = a["kv_bytes"] + a["qo_bytes"] // 2 + a["part_bytes"]
         res["decode_attn_GBps"] = round(attn_bytes / (t["attn"] * 1e-3) / 1e9, 1)
         res["decode_attn_hbm_frac"] = round(res["decode_attn_GBps"] / HBM_PEAK_GBPS, 4)
+        if peaks:
+            res["decode_attn_frac_of_measured_read"] = round(
+                res["decode_attn_GBps"] / peaks["stream_read_GBps"], 4)
     return res
 
 
@@ -278,6 +350,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     msa.load()
+    print("[bench] measured peaks", file=sys.stderr, flush=True)
+    peaks = measured_peaks()
     order = [int(x) for x in args.workloads.split(",") if x]
     main_cfg = order[0]
     results = {}
@@ -286,7 +360,7 @@ def main():
         steps = args.steps if cfg == main_cfg else max(5, min(args.steps, 20))
         print(f"[bench] workload {cfg}: {steps} steps", file=sys.stderr, flush=True)
         case, r = run_workload(cfg, steps, args.warmup, graph_replay=not args.eager_only)
-        results[cfg] = summarize(cfg, case, r)
+        results[cfg] = summarize(cfg, case, r, peaks)
         if cfg == main_cfg:
             main_case, main_run = case, r
         else:
@@ -310,7 +384,8 @@ def main():
     roofline = dict(kernel="index_score_stream_kernel", bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
                     traffic=traffic_from_profile(), alg_bytes_per_launch=a["score_bytes"],
-                    avg_launch_us=round(t_score * 1e3, 2))
+                    avg_launch_us=round(t_score * 1e3, 2),
+                    frac_of_measured_read=round(achieved / peaks["stream_read_GBps"], 4))
     cpu = None
     if not args.no_cpu_baseline and main_case is not None and not main_case.prefill:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -321,6 +396,9 @@ def main():
         warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4),
         launch=("eager four-call step" if args.eager_only else
                 "hip graph replay of the four-call step (eager ms_per_step also reported)"),
+        timing=("sum over the steps of one HIP event pair around each step; an untimed "
+                "1 GiB read before every step leaves L2 and MALL cold"),
+        warm_cache_ms_per_step=m.get("warm_cache_ms_per_step"),
         eager_ms_per_step=round(main_run["eager_ms_per_step"], 4), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=main_case.name, batch=main_case.rows,
@@ -328,6 +406,7 @@ def main():
                     head_dim=main_case.D, n_idx=main_case.n_idx, d_idx=main_case.d_idx,
                     top_k=main_case.k, paged=True, parallelism="none (1 GPU)"),
         index_scan_GBps=m.get("index_scan_GBps"), roofline=roofline, cpu_baseline=cpu,
+        measured_peaks=peaks,
         device=torch.cuda.get_device_name(0),
         workloads={results[c]["workload"]: results[c] for c in order})
     print(json.dumps(line))

@@ -10,6 +10,8 @@ Calls (same names and meaning as the C functions):
     msa_index_score, msa_topk_blocks, msa_build_page_table, msa_topk_blocks_paged,
     msa_sparse_attn_decode, msa_prefill_workspace_size, msa_sparse_attn_prefill,
     msa_lse_merge, msa_version
+Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
+    msa_peak_stream_read, msa_peak_mfma_bf16
 """
 from .binding import (  # noqa: F401
     Dims,
@@ -20,6 +22,8 @@ from .binding import (  # noqa: F401
     msa_build_page_table,
     msa_index_score,
     msa_lse_merge,
+    msa_peak_mfma_bf16,
+    msa_peak_stream_read,
     msa_prefill_workspace_size,
     msa_sparse_attn_decode,
     msa_sparse_attn_prefill,

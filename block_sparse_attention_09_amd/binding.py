@@ -53,6 +53,8 @@ _SIGS = {
     "msa_sparse_attn_prefill": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
                                 ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
     "msa_lse_merge": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P],
+    "msa_peak_stream_read": [_P, ctypes.c_size_t, _P, _P],
+    "msa_peak_mfma_bf16": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
 }
 
 _lib = None
@@ -254,3 +256,21 @@ def msa_lse_merge(o_part, lse_part, o=None, lse=None, stream=None):
     _check(load().msa_lse_merge(rows, H, nslot, D, _ptr(o_part), _ptr(lse_part), _ptr(o),
                                 _ptr(lse), _stream(stream)), "msa_lse_merge")
     return o, lse
+
+
+def msa_peak_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Launch the streaming-read probe over every byte of `buf` (include/msa_peaks.h)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _need(sink, torch.float32, "sink")
+    _check(load().msa_peak_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                       _stream(stream)), "msa_peak_stream_read")
+
+
+def msa_peak_mfma_bf16(iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch the bf16 matrix-core loop probe; returns the FLOPs it performs."""
+    _need(sink, torch.float32, "sink")
+    flops = ctypes.c_double(0.0)
+    _check(load().msa_peak_mfma_bf16(iters, _ptr(sink), ctypes.byref(flops), _stream(stream)),
+           "msa_peak_mfma_bf16")
+    return flops.value

@@ -9,35 +9,45 @@
 //
 // Score of block b for (row, group):  max over visible tokens t of
 //     sum_j q_j . k_t / sqrt(d_idx)
-// computed here as qbar . k_t with qbar = sum_j q_j formed in fp32 and split
-// into bf16 hi + lo halves (hi = bf16(qbar), lo = bf16(qbar - hi)), so two bf16
-// MFMA passes give qbar . k with a relative error near 2^-17 per term against
-// the exact sum, accumulated in fp32.  Max commutes with the positive scale,
-// which is applied once per block.
+// computed here as qbar . k_t with qbar = sum_j q_j formed in fp32, products
+// and sums in fp32 fused multiply-adds (rounding near 2^-24 per operation).
+// Max commutes with the positive scale, which is applied once per block.
 //
 // Streaming kernel (decode shape: every row reads its own pages).  Each wave
 // takes an equal slice of the scored blocks of all (row, group) pairs and
 // walks its segments half a block (64 tokens) per step with the next step's
-// loads in flight while the current one runs on the matrix cores.  Each lane
-// loads 16 contiguous bytes straight into the MFMA A operand (token = M index,
-// 32 dims = K), so the key index goes HBM -> VGPR with no LDS round trip; B
-// holds qbar hi/lo in column 0 only.  The prefill shape (many rows of one
-// request) uses the row-tiled kernel in index_score_tiled.hip instead.
+// loads in flight while the current one is reduced.  At about one flop per
+// byte the scan is bound by HBM, not by arithmetic, so the shape of the loads
+// decides its speed: every load instruction of a wave reads whole 256-byte
+// token rows (16 lanes x 16 B per row for d_idx 128), which streams at about
+// 6.9 TB/s on MI355X, where the 16-token x 64-byte pieces an MFMA operand
+// load takes reach about 5.8.  So the dot products run on the vector ALUs
+// (eight FMAs per lane per row piece, then a four-step DPP butterfly across
+// the row's lanes), which keep up with the stream with room to spare.  The
+// prefill shape (many rows of one request share each key block, a dense
+// contraction) uses the matrix-core kernel in index_score_tiled.hip instead.
 #include "msa_internal.h"
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace msa {
 
 namespace {
 
-constexpr int kTilesPerStep = 4;   // 4 x 16 tokens = half a block per register buffer
 constexpr int kMaxChunk = 64;      // chunk length bound: one page id per lane
 
+// Half a block (64 tokens) of key index in registers: load j of the wave moves
+// 1 KB, tokens 64 h + TPL j + l / CH (TPL = 64 / CH tokens per load), lane l
+// holding dims 8 (l % CH) .. + 8 of its token (CH = d_idx / 8 lanes per token
+// row), so every load instruction reads whole token rows.
 template <int DIDX>
 struct StepBuf {
-    bf16x8 a[kTilesPerStep][DIDX / 32];
+    static constexpr int CH = DIDX / 8;
+    static constexpr int TPL = kWave / CH;
+    static constexpr int NLD = 64 / TPL;
+    u32x4 v[NLD];
 };
 
 // Key-index stream: read once, never reused -> non-temporal loads.
@@ -48,33 +58,45 @@ __device__ __forceinline__ u32x4 ld16_stream(const bf16_t *p) {
 template <int DIDX>
 __device__ __forceinline__ void load_step(StepBuf<DIDX> &buf, const bf16_t *page_base, int64_t kts,
                                           int half, int lane) {
-    const int kq = (lane >> 4) * 8;
+    using B = StepBuf<DIDX>;
+    const bf16_t *p = page_base + (int64_t)(64 * half + lane / B::CH) * kts + 8 * (lane % B::CH);
 #pragma unroll
-    for (int ti = 0; ti < kTilesPerStep; ++ti) {
-        const int tok = (half * kTilesPerStep + ti) * 16 + (lane & 15);
-        const bf16_t *p = page_base + (int64_t)tok * kts + kq;
-#pragma unroll
-        for (int c = 0; c < DIDX / 32; ++c) buf.a[ti][c] = as_bf16x8(ld16_stream(p + 32 * c));
-    }
+    for (int j = 0; j < B::NLD; ++j) buf.v[j] = ld16_stream(p + (int64_t)(B::TPL * j) * kts);
+}
+
+// x summed over the CH lanes of a token row, returned in every one of them
+// (butterflies over lane partners l ^ 15, l ^ 7, l ^ 2, l ^ 1 within the row,
+// each one DPP-fed add; CH = 8 skips the first).
+template <int CH>
+__device__ __forceinline__ float row_sum(float x) {
+    auto dpp_add = [](float v, auto ctrl) {
+        return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                              0xf, 0xf, false));
+    };
+    if constexpr (CH == 16) x = dpp_add(x, std::integral_constant<int, 0x140>{});  // row_mirror
+    x = dpp_add(x, std::integral_constant<int, 0x141>{});                          // row_half_mirror
+    x = dpp_add(x, std::integral_constant<int, 0x4e>{});                           // quad_perm 2,3,0,1
+    x = dpp_add(x, std::integral_constant<int, 0xb1>{});                           // quad_perm 1,0,3,2
+    return x;
 }
 
 // Max over the 64 tokens of one half block of qbar . k_t (fp32), tokens after
-// pos masked.  tok_base is the position of this lane's first accumulator row.
+// pos masked.  tok is the position of this lane's token in the first load.
 template <int DIDX>
-__device__ __forceinline__ float block_half_max(const StepBuf<DIDX> &buf, const bf16x8 *bhi,
-                                                const bf16x8 *blo, int tok_base, int pos) {
+__device__ __forceinline__ float block_half_max(const StepBuf<DIDX> &buf, const float *qv, int tok,
+                                                int pos) {
+    using B = StepBuf<DIDX>;
     float best = -INFINITY;
 #pragma unroll
-    for (int ti = 0; ti < kTilesPerStep; ++ti) {
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < B::NLD; ++j) {
+        float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < DIDX / 32; ++c) {
-            d = mfma16(buf.a[ti][c], bhi[c], d);
-            d = mfma16(buf.a[ti][c], blo[c], d);
+        for (int e = 0; e < 4; ++e) {
+            s = fmaf(qv[2 * e], bf16_lo(buf.v[j][e]), s);
+            s = fmaf(qv[2 * e + 1], bf16_hi(buf.v[j][e]), s);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            best = fmaxf(best, (tok_base + ti * 16 + i <= pos) ? d[i] : -INFINITY);
+        s = row_sum<B::CH>(s);
+        best = fmaxf(best, (tok + B::TPL * j <= pos) ? s : -INFINITY);
     }
     return best;
 }
@@ -114,67 +136,38 @@ __device__ __forceinline__ void score_segment(const PairInfo &pi, int b_beg, int
     // the pages of the first (up to 64) blocks and the query index vectors in
     // one round trip
     const int my_page = (lane < b_end - b_beg) ? bt[b_beg + lane] : 0;
-    const int kq = (lane >> 4) * 8;
-    const bool col0 = (lane & 15) == 0;
-    const bf16_t *qb = q_idx + ((int64_t)pi.r * G + pi.g) * n_idx * DIDX + kq;
-    float acc[DIDX / 32][8];
-#pragma unroll
-    for (int c = 0; c < DIDX / 32; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-    for (int j0 = 0; j0 < n_idx; j0 += 4) {
-        u32x4 w[4][DIDX / 32];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int c = 0; c < DIDX / 32; ++c)
-                w[jj][c] = (j0 + jj < n_idx) ? ld16(qb + (j0 + jj) * DIDX + 32 * c) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int c = 0; c < DIDX / 32; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[c][2 * e] += bf16_lo(w[jj][c][e]);
-                    acc[c][2 * e + 1] += bf16_hi(w[jj][c][e]);
-                }
-    }
-    // qbar in fp32 -> bf16 hi + lo, placed in B column 0 (lanes 0, 16, 32, 48).
-    bf16x8 bhi[DIDX / 32], blo[DIDX / 32];
-#pragma unroll
-    for (int c = 0; c < DIDX / 32; ++c) {
-        u32x4 hw, lw;
+    // qbar = sum_j q_j in fp32: this lane's 8 dims, 8 (l % CH) .. + 8
+    using B = StepBuf<DIDX>;
+    const bf16_t *qb = q_idx + ((int64_t)pi.r * G + pi.g) * n_idx * DIDX + 8 * (lane % B::CH);
+    float qv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < n_idx; ++j) {
+        const u32x4 w = ld16(qb + j * DIDX);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t h0 = f32_to_bf16_rne(acc[c][2 * e]);
-            const uint32_t h1 = f32_to_bf16_rne(acc[c][2 * e + 1]);
-            const uint32_t l0 = f32_to_bf16_rne(acc[c][2 * e] - __uint_as_float(h0 << 16));
-            const uint32_t l1 = f32_to_bf16_rne(acc[c][2 * e + 1] - __uint_as_float(h1 << 16));
-            hw[e] = col0 ? (h0 | (h1 << 16)) : 0u;
-            lw[e] = col0 ? (l0 | (l1 << 16)) : 0u;
+            qv[2 * e] += bf16_lo(w[e]);
+            qv[2 * e + 1] += bf16_hi(w[e]);
         }
-        bhi[c] = as_bf16x8(hw);
-        blo[c] = as_bf16x8(lw);
     }
 
     const int64_t gofs = (int64_t)pi.g * kgs;
     const int nblk = b_end - b_beg;
     // Two register buffers, one per half block (static indices: no scratch).
     // The loads of the next half (or of the next block's page) are issued
-    // before the matrix-core work on the current half.
+    // before the current half is reduced.
     StepBuf<DIDX> bufA, bufB;
     const bf16_t *page = kbase + (int64_t)__builtin_amdgcn_readlane(my_page, 0) * kps + gofs;
     load_step<DIDX>(bufA, page, kts, 0, lane);
     for (int bi = 0; bi < nblk; ++bi) {
-        const int tok_base = (b_beg + bi) * kBlk + (lane >> 4) * 4;
+        const int tok = (b_beg + bi) * kBlk + lane / B::CH;
         load_step<DIDX>(bufB, page, kts, 1, lane);
-        float best = block_half_max<DIDX>(bufA, bhi, blo, tok_base, pi.pos);
+        float best = block_half_max<DIDX>(bufA, qv, tok, pi.pos);
         if (bi + 1 < nblk) {
             page = kbase + (int64_t)__builtin_amdgcn_readlane(my_page, bi + 1) * kps + gofs;
             load_step<DIDX>(bufA, page, kts, 0, lane);
         }
-        best = fmaxf(best, block_half_max<DIDX>(bufB, bhi, blo, tok_base + 64, pi.pos));
-        // column 0 of the accumulators lives in lanes 0, 16, 32, 48
+        best = fmaxf(best, block_half_max<DIDX>(bufB, qv, tok + 64, pi.pos));
+        // the token rows of a load are the lane groups of CH lanes
+        if (B::CH == 8) best = wave_max_xor(best, 8);
         best = wave_max_xor(best, 16);
         best = wave_max_xor(best, 32);
         if (lane == 0) out[b_beg + bi] = best * scale;

@@ -10,6 +10,7 @@
 
 #include "msa.h"
 #include "msa_internal.h"
+#include "msa_peaks.h"
 
 namespace {
 
@@ -281,6 +282,23 @@ msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D, co
                                             lse_part, static_cast<msa::bf16_t *>(o), lse,
                                             as_stream(stream)),
                       "msa_lse_merge");
+}
+
+msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
+                                  msa_stream_t stream) {
+    REQUIRE(bytes % 16 == 0, MSA_ERR_INVALID, "bytes = %zu must be a multiple of 16", bytes);
+    if (bytes == 0) return ok();
+    REQUIRE(buf && sink, MSA_ERR_NULL, "buf and sink are required");
+    REQUIRE(aligned(buf, 16), MSA_ERR_INVALID, "buf must be 16-byte aligned");
+    return hip_status(msa::launch_peak_stream_read(buf, (int64_t)bytes, sink, as_stream(stream)),
+                      "msa_peak_stream_read");
+}
+
+msa_status_t msa_peak_mfma_bf16(int32_t iters, float *sink, double *flops, msa_stream_t stream) {
+    REQUIRE(iters >= 1, MSA_ERR_INVALID, "iters = %d must be >= 1", iters);
+    REQUIRE(sink && flops, MSA_ERR_NULL, "sink and flops are required");
+    return hip_status(msa::launch_peak_mfma_bf16(iters, sink, flops, as_stream(stream)),
+                      "msa_peak_mfma_bf16");
 }
 
 }  // extern "C"

@@ -109,4 +109,9 @@ hipError_t launch_attn_prefill(const AttnArgs &a, int num_pages, void *workspace
 hipError_t launch_lse_merge(int rows, int H, int nslot, const bf16_t *o_part,
                             const float *lse_part, bf16_t *o, float *lse, hipStream_t stream);
 
+// measured-peak probes (not part of the MSA path)
+hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
+                                   hipStream_t stream);
+hipError_t launch_peak_mfma_bf16(int iters, float *sink, double *flops, hipStream_t stream);
+
 }  // namespace msa

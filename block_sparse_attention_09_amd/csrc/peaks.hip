@@ -1,0 +1,87 @@
+// peaks.hip -- measured machine peaks (gfx950), the reference points the MSA
+// kernels' rooflines are read against besides the published ones: a plain
+// streaming read of a large buffer (HBM) and a register-resident bf16 MFMA
+// loop (matrix cores).  Neither is part of the MSA path.
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kPeakThreads = 256;
+
+// Workgroup w reads the contiguous 64 KB chunk w of the buffer, every thread
+// keeping eight non-temporal 16-B loads in flight (the fastest of the grid
+// shapes and depths tried on MI355X), and folds what it read into one word;
+// the fold is stored only if it equals a value no sane input produces, which
+// keeps every load alive at the cost of nothing.
+constexpr int64_t kReadChunk16 = (64 << 10) / 16;  // 16-B units per workgroup
+constexpr int kReadDepth = 8;
+
+__global__ __launch_bounds__(kPeakThreads) void stream_read_kernel(const u32x4 *__restrict__ p,
+                                                                   int64_t n16,
+                                                                   float *__restrict__ sink) {
+    const int64_t b = (int64_t)blockIdx.x * kReadChunk16;
+    const int64_t e = b + kReadChunk16 < n16 ? b + kReadChunk16 : n16;
+    uint32_t acc = 0u;
+    int64_t i = b + threadIdx.x;
+    for (; i + (kReadDepth - 1) * kPeakThreads < e; i += kReadDepth * kPeakThreads) {
+        u32x4 v[kReadDepth];
+#pragma unroll
+        for (int k = 0; k < kReadDepth; ++k)
+            v[k] = __builtin_nontemporal_load(p + i + k * kPeakThreads);
+#pragma unroll
+        for (int k = 0; k < kReadDepth; ++k) acc += v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
+    for (; i < e; i += kPeakThreads) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    if (acc == 0x9e3779b9u) sink[0] = __uint_as_float(acc);
+}
+
+// Four independent 32x32x16 bf16 accumulation chains per wave, operands in
+// registers: the matrix-core rate with nothing else in the way.
+__global__ __launch_bounds__(kPeakThreads) void mfma_loop_kernel(int iters,
+                                                                 float *__restrict__ sink) {
+    bf16x8 a, b[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(0.001f * (float)threadIdx.x + (float)e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j][e] = (__bf16)(0.5f * (float)e - (float)j);
+    }
+    f32x16 c[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = mfma32(a, b[j], c[j]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += c[j][j];
+    if (s == 1.2345f) sink[0] = s;
+}
+
+}  // namespace
+
+hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
+                                   hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    const int64_t grid = (n16 + kReadChunk16 - 1) / kReadChunk16;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kPeakThreads), 0, stream,
+                       static_cast<const u32x4 *>(buf), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_peak_mfma_bf16(int iters, float *sink, double *flops, hipStream_t stream) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = 2 * cus;  // two workgroups per CU: two waves per SIMD
+    *flops = (double)grid * (kPeakThreads / kWave) * (double)iters * 4.0 * (2.0 * 32 * 32 * 16);
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(kPeakThreads), 0, stream, iters, sink);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,42 @@
+/*
+ * msa_peaks.h -- measured machine peaks for libmsa's roofline reports.
+ *
+ * The MSA kernels are read against the published MI355X peaks (8 TB/s HBM,
+ * 2.5 PFLOP/s dense bf16) and against what this device actually sustains with
+ * nothing else in the way.  These two probes measure the latter; they are
+ * measurement aids, not steps of the MSA path, and follow the conventions of
+ * msa.h (status codes, msa_last_error(), asynchronous on the caller's stream,
+ * no allocation, device pointers unless stated).
+ */
+#ifndef MSA_PEAKS_H_
+#define MSA_PEAKS_H_
+
+#include "msa.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming read of `bytes` bytes at `buf` (device, 16-byte aligned, bytes a
+ * multiple of 16), every byte once: one 256-thread workgroup per 64 KB chunk,
+ * each thread keeping eight non-temporal 16-byte loads in flight.  `sink` (device, one float) is written only in a case no
+ * real data reaches; it keeps the loads from being optimised away.  Time the
+ * launch with events around it: bytes / time is the sustained HBM read rate
+ * (use a buffer much larger than the 256 MB last-level cache).
+ * Errors: MSA_ERR_INVALID (alignment, size), MSA_ERR_NULL, MSA_ERR_HIP. */
+msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
+                                  msa_stream_t stream);
+
+/* Register-resident bf16 matrix-core loop: two 256-thread workgroups per CU,
+ * each wave runs `iters` iterations of four independent 32x32x16 bf16 MFMA
+ * accumulation chains.  *flops (host) receives the floating-point operations the
+ * launch performs (2 * 32 * 32 * 16 per MFMA); flops / time is the sustained
+ * dense bf16 rate.  `sink` as above.
+ * Errors: MSA_ERR_INVALID (iters < 1), MSA_ERR_NULL, MSA_ERR_HIP. */
+msa_status_t msa_peak_mfma_bf16(int32_t iters, float *sink, double *flops, msa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_PEAKS_H_ */

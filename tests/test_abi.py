@@ -9,6 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msa.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 MSA_OK, MSA_ERR_NULL, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE = 0, 1, 2, 3, 4
 
@@ -22,14 +24,14 @@ def lib():
     return binding.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(headers=None):
+    text = "".join(open(h).read() for h in (headers or HEADERS))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
 
 
 def test_header_declares_the_six_calls():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
               "msa_sparse_attn_decode", "msa_sparse_attn_prefill", "msa_lse_merge"):
         assert f in names
@@ -157,6 +159,17 @@ def test_merge_validation(lib):
     assert lib.msa_lse_merge(1, 0, 3, 128, FAKE, FAKE, FAKE, None, None) == MSA_ERR_INVALID
     assert lib.msa_lse_merge(1, 8, 3, 128, None, FAKE, FAKE, None, None) == MSA_ERR_NULL
     assert lib.msa_lse_merge(0, 8, 3, 128, None, None, None, None, None) == MSA_OK
+
+
+def test_peak_probe_validation(lib):
+    flops = ctypes.c_double(0.0)
+    assert lib.msa_peak_stream_read(FAKE, 24, FAKE, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_stream_read(MISALIGNED, 32, FAKE, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_stream_read(None, 32, FAKE, None) == MSA_ERR_NULL
+    assert lib.msa_peak_stream_read(None, 0, None, None) == MSA_OK
+    assert lib.msa_peak_mfma_bf16(0, FAKE, ctypes.byref(flops), None) == MSA_ERR_INVALID
+    assert lib.msa_peak_mfma_bf16(8, None, ctypes.byref(flops), None) == MSA_ERR_NULL
+    assert lib.msa_peak_mfma_bf16(8, FAKE, None, None) == MSA_ERR_NULL
 
 
 def test_binding_refuses_host_tensors():
