@@ -1,0 +1,46 @@
+"""GPU checks of the measured-peak probes (include/msa_peaks.h): they run,
+report the work they did, and land in a plausible range for one MI355X.  The
+bounds are loose on purpose: they catch a probe that reads nothing or issues
+no matrix work, not a slow machine."""
+import pytest
+import torch
+
+import block_sparse_attention_09_amd as msa
+
+pytestmark = pytest.mark.gpu
+
+
+def _time(fn, reps=3):
+    fn()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    return best
+
+
+def test_stream_read_probe():
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    # a size that is not a multiple of the 64 KB workgroup chunk: ragged last chunk
+    buf = torch.ones((1 << 30) // 4 + 4 * 37, dtype=torch.float32, device="cuda")
+    ms = _time(lambda: msa.msa_peak_stream_read(buf, sink))
+    gbps = buf.numel() * 4 / (ms * 1e-3) / 1e9
+    assert 1000.0 < gbps < 8200.0, gbps
+    assert sink.item() == 0.0  # the fold never matches the guard value on this data
+
+
+def test_mfma_probe():
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    iters = 2048
+    flops = msa.msa_peak_mfma_bf16(iters, sink)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == 2 * cus * 4 * iters * 4 * (2 * 32 * 32 * 16)
+    ms = _time(lambda: msa.msa_peak_mfma_bf16(iters, sink))
+    tflops = flops / (ms * 1e-3) / 1e12
+    assert 200.0 < tflops < 2600.0, tflops
