@@ -54,11 +54,32 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v combined with its value in lane l ^ mask, the result in every lane.  For
+// mask 16 and 32 the partner values come from the gfx950 lane-swap VALU ops
+// (v_permlane16_swap exchanges the odd 16-lane rows of one operand with the even
+// rows of the other, v_permlane32_swap the upper half of one with the lower half
+// of the other: with both operands v, the two results hold v and v at l ^ mask),
+// which stay off the LDS pipe that a bpermute shuffle goes through; both lanes
+// of a pair combine the same two values, so they agree bit for bit.
+__device__ __forceinline__ float2 xor_partners(float v, int mask) {
+    const uint32_t u = __float_as_uint(v);
+    if (mask == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return make_float2(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    if (mask == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return make_float2(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    return make_float2(v, __shfl_xor(v, mask, kWave));
+}
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
-    return fmaxf(v, __shfl_xor(v, mask, kWave));
+    const float2 p = xor_partners(v, mask);
+    return fmaxf(p.x, p.y);
 }
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) {
-    return v + __shfl_xor(v, mask, kWave);
+    const float2 p = xor_partners(v, mask);
+    return p.x + p.y;
 }
 
 // ---------------------------------------------------------------- launchers
