@@ -43,6 +43,10 @@ constexpr int KST = 136;  // LDS row stride (bf16 elements): 272 B keeps rows of
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Output stage of a block-major wave: 8 partial rows of 128 dims, padded by
+// 16 bytes so that the 8 rows written at once fall in different LDS banks.
+constexpr int kStageRow = 128 + 8;
+
 struct AttnSmem {
     bf16_t k[kBlk * KST];   // K page, [token][dim]
     bf16_t vt[128 * KST];   // V page, [dim][permuted token position]
@@ -131,7 +135,8 @@ struct TileMeta {
 // Lane l owns query row l % 32 of the tile; lane half h = l / 32 picks which
 // tokens (S^T rows) and head dimensions (O^T rows) it holds.
 template <int HG>
-__device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, const AttnArgs &a, int g,
+__device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *ostage,
+                                                const AttnArgs &a, int g,
                                                 const int32_t *__restrict__ lst, int nq,
                                                 float scale_log2) {
     constexpr int QPT = 32 / HG;  // query tokens per tile
@@ -256,11 +261,13 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, const AttnAr
         // normalised partial: element 4 q + r of o[dt] is dim 32 dt + 8 q + 4 h + r.
         // One lane-half swap per packed pair gives each lane 8 contiguous dims
         // twice per 32-dim tile (lower half: 0..7 and 16..23, upper: 8..15 and
-        // 24..31), so every 16-byte store fills 32 contiguous bytes of a row.
-        if (meta.valid) {
+        // 24..31).  The rows then pass through this wave's LDS stage, 8 rows at a
+        // time, so that every global store writes 4 whole 256-byte rows: stores
+        // that cover a row in 32-byte pieces from 32 rows at once sustain about
+        // 3.0 TB/s on random rows, whole rows about 5.0.
+        {
             const float inv = 1.f / l;
-            const int64_t oi = ((int64_t)meta.row * H + g * HG + hh) * a.nslot + meta.slot;
-            bf16_t *op = a.o_part + oi * 128 + 8 * h;
+            u32x4 cw[4][2];
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 uint32_t pk[4][2];  // [q][pair]: dims 8 q + 4 h + {0,1}, {2,3}
@@ -270,20 +277,44 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, const AttnAr
                     pk[q][1] = pack_bf16x2(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv);
                 }
                 // A = q 0 and 2 (kept by the lower half), B = q 1 and 3 (kept by the upper)
-                u32x4 c0, c1;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const auto x = __builtin_amdgcn_permlane32_swap(pk[0][i], pk[1][i], false, false);
                     const auto y = __builtin_amdgcn_permlane32_swap(pk[2][i], pk[3][i], false, false);
-                    c0[i] = x[0];
-                    c0[2 + i] = x[1];
-                    c1[i] = y[0];
-                    c1[2 + i] = y[1];
+                    cw[dt][0][i] = x[0];
+                    cw[dt][0][2 + i] = x[1];
+                    cw[dt][1][i] = y[0];
+                    cw[dt][1][2 + i] = y[1];
                 }
-                *reinterpret_cast<u32x4 *>(op + 32 * dt) = c0;
-                *reinterpret_cast<u32x4 *>(op + 32 * dt + 16) = c1;
             }
-            if (h == 0) a.lse_part[oi] = (mx * scale_log2 + __builtin_amdgcn_logf(l)) * kLn2;
+            const int64_t oi = ((int64_t)meta.row * H + g * HG + hh) * a.nslot + meta.slot;
+            const int oi_lo = (int)(uint32_t)oi, oi_hi = (int)(oi >> 32);
+            const int ok = meta.valid ? 1 : 0;
+#pragma unroll
+            for (int rho = 0; rho < 4; ++rho) {
+                if ((j >> 3) == rho) {
+                    bf16_t *sr = ostage + (j & 7) * kStageRow + 8 * h;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        *reinterpret_cast<u32x4 *>(sr + 32 * dt) = cw[dt][0];
+                        *reinterpret_cast<u32x4 *>(sr + 32 * dt + 16) = cw[dt][1];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int rr = 4 * i + (lane >> 4);  // stage row; tile row 8 rho + rr
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(ostage + rr * kStageRow +
+                                                                     8 * (lane & 15));
+                    const int src = 8 * rho + rr;  // lanes src and src + 32 hold its metadata
+                    const int lo = __shfl(oi_lo, src, kWave), hi = __shfl(oi_hi, src, kWave);
+                    if (__shfl(ok, src, kWave)) {
+                        const int64_t ro = ((int64_t)hi << 32) | (uint32_t)lo;
+                        *reinterpret_cast<u32x4 *>(a.o_part + ro * 128 + 8 * (lane & 15)) = v;
+                    }
+                }
+            }
+            if (meta.valid && h == 0)
+                a.lse_part[oi] = (mx * scale_log2 + __builtin_amdgcn_logf(l)) * kLn2;
         }
         meta = meta_next;
     }
@@ -447,6 +478,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_blockmajor_kernel(
     AttnArgs a, const int32_t *__restrict__ offs, const int32_t *__restrict__ list,
     float scale_log2) {
     __shared__ AttnSmem sm;
+    __shared__ __attribute__((aligned(16))) bf16_t ostage[kAttnWaves][8 * kStageRow];
     __shared__ int last_tok;
     const int64_t u = blockIdx.x;  // page * G + group
     const int o0 = offs[u], nq = offs[u + 1] - o0;
@@ -472,7 +504,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_blockmajor_kernel(
     __syncthreads();
     stage_kv_store(sm, st, last_tok);
     __syncthreads();
-    blockmajor_wave<HG>(sm, a, g, list + o0, nq, scale_log2);
+    blockmajor_wave<HG>(sm, &ostage[threadIdx.x >> 6][0], a, g, list + o0, nq, scale_log2);
 }
 
 // ------------------------------------------------------------------ decode
