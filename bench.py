@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workloads", default="2,5,3,4,1",
                     help="comma list of workload ids; the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv-on-host", action="store_true",
+                    help="skip the extra run of the headline workload with K/V in pinned host memory")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain 1-read/1-write fp32 elementwise kernel over this "
                          "many MiB (reference for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
@@ -83,12 +85,19 @@ def algorithmic(case, sel=None):
     return out
 
 
-def run_workload(cfg, steps, warmup, graph_replay=True):
+def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     import torch
     import block_sparse_attention_09_amd as msa
     import msa_synth
 
     case = msa_synth.config_case(cfg, device="cuda")
+    if kv_on_host:
+        # decoupled offload: key index on the GPU, K/V in pinned host memory,
+        # read by the attention kernel page by page as the selection names them
+        case.k_cache = case.k_cache.cpu().pin_memory()
+        case.v_cache = case.v_cache.cpu().pin_memory()
+        case.name += "-kv-on-host"
+        torch.cuda.empty_cache()
     d = msa.Dims(G=case.G, Hg=case.Hg, D=case.D, n_idx=case.n_idx, d_idx=case.d_idx, blk=128)
     scale = 1.0 / math.sqrt(case.D)
     dev = case.q.device
@@ -367,6 +376,17 @@ def main():
             del case
             torch.cuda.empty_cache()
 
+    if not args.no_kv_on_host and not args.eager_only:
+        print(f"[bench] workload {main_cfg} with K/V in pinned host memory", file=sys.stderr,
+              flush=True)
+        case, r = run_workload(main_cfg, 20, args.warmup, kv_on_host=True)
+        res = summarize(main_cfg, case, r, peaks)
+        a, t = r["alg"], r["per_call_ms"]
+        res["host_link_attn_GBps"] = round(a["kv_bytes"] / (t["attn"] * 1e-3) / 1e9, 1)
+        results["kv-on-host"] = res
+        del case
+        torch.cuda.empty_cache()
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.zeros(n // 4, dtype=torch.float32, device="cuda")
@@ -408,7 +428,7 @@ def main():
         index_scan_GBps=m.get("index_scan_GBps"), roofline=roofline, cpu_baseline=cpu,
         measured_peaks=peaks,
         device=torch.cuda.get_device_name(0),
-        workloads={results[c]["workload"]: results[c] for c in order})
+        workloads={results[c]["workload"]: results[c] for c in results})
     print(json.dumps(line))
 
 

@@ -115,10 +115,18 @@ def _need(t: torch.Tensor, dtype, name, contiguous=False):
         raise ValueError(f"{name} must be contiguous")
 
 
-def view_of(cache: torch.Tensor) -> View:
+def view_of(cache: torch.Tensor, host_ok: bool = False) -> View:
     """C view of a 4-d bf16 cache tensor indexed [page][group][token][dim]
-    (any strides, dim stride 1)."""
-    _need(cache, torch.bfloat16, "cache")
+    (any strides, dim stride 1).  With host_ok, a pinned host tensor is accepted
+    as well: pinned host memory is mapped into the device's address space, so
+    the attention kernels read the selected pages from it directly."""
+    if host_ok and not cache.is_cuda:
+        if cache.dtype != torch.bfloat16:
+            raise TypeError(f"cache: expected torch.bfloat16, got {cache.dtype}")
+        if not cache.is_pinned():
+            raise TypeError("cache: a host cache must be pinned (pin_memory) to be device-mapped")
+    else:
+        _need(cache, torch.bfloat16, "cache")
     if cache.dim() != 4 or cache.stride(3) != 1:
         raise ValueError("cache must be 4-d [page][group][token][dim] with unit dim stride")
     return View(cache.data_ptr(), cache.stride(0), cache.stride(1), cache.stride(2))
@@ -210,9 +218,9 @@ def msa_sparse_attn_decode(dims: Dims, q, k_cache, v_cache, sel, page_table, row
     nslot = sel.shape[2]
     o_part, lse_part = _attn_out(q, nslot, o_part, lse_part)
     scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dims.D))
-    _check(load().msa_sparse_attn_decode(ctypes.byref(dims), q.shape[0], _ptr(q),
-                                         view_of(k_cache), view_of(v_cache), _ptr(sel),
-                                         _ptr(page_table), nslot, _ptr(row_pos), scale,
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_sparse_attn_decode(ctypes.byref(dims), q.shape[0], _ptr(q), kv[0], kv[1],
+                                         _ptr(sel), _ptr(page_table), nslot, _ptr(row_pos), scale,
                                          _ptr(o_part), _ptr(lse_part), _stream(stream)),
            "msa_sparse_attn_decode")
     return o_part, lse_part
@@ -236,9 +244,10 @@ def msa_sparse_attn_prefill(dims: Dims, q, k_cache, v_cache, sel, page_table, ro
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dims.D))
-    _check(load().msa_sparse_attn_prefill(ctypes.byref(dims), rows, _ptr(q),
-                                          view_of(k_cache), view_of(v_cache), _ptr(sel),
-                                          _ptr(page_table), nslot, _ptr(row_pos), num_pages,
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_sparse_attn_prefill(ctypes.byref(dims), rows, _ptr(q), kv[0], kv[1],
+                                          _ptr(sel), _ptr(page_table), nslot, _ptr(row_pos),
+                                          num_pages,
                                           scale, _ptr(workspace), workspace.numel(),
                                           _ptr(o_part), _ptr(lse_part), _stream(stream)),
            "msa_sparse_attn_prefill")

@@ -72,7 +72,15 @@ typedef struct {
  * and every stride a multiple of 8.  The default layout [page][G][128][dim]
  * is page_stride = G*128*dim, group_stride = 128*dim, token_stride = dim; a
  * token-major cache [page][128][G][dim] is group_stride = dim,
- * token_stride = G*dim. */
+ * token_stride = G*dim.
+ *
+ * The K and V caches of the attention calls may also live in pinned host
+ * memory that is mapped into the device's address space (hipHostMalloc'd,
+ * torch pin_memory): the kernels then read only the pages the selection names,
+ * over the host link.  This is the pages' decoupled offload (未来工作 of the
+ * aihot.news page): the full key index resident on the GPU, the KV cache in
+ * CPU memory, loaded on demand from the top-k selection.  Results are
+ * identical to a device-resident cache; the time is bound by the host link. */
 typedef struct {
     const void *base;
     int64_t page_stride, group_stride, token_stride;

@@ -257,6 +257,42 @@ def test_deterministic_and_placement_invariant():
         assert torch.equal(a[key], d[key]), key
 
 
+def test_kv_cache_in_pinned_host_memory():
+    """Decoupled offload: the key index stays on the GPU, K and V live in pinned
+    host memory and the attention kernels read only the selected pages over the
+    host link; results are bit-identical to a device-resident cache, for decode
+    and for the block-major prefill."""
+    for prefill in (False, True):
+        print(f"[case] kv cache in pinned host memory, prefill={prefill}", flush=True)
+        if prefill:
+            case = _build(seed=311, ctx_lens=[1500], G=2, Hg=8, d_idx=128, k=3,
+                          prefill_rows=300, poison="nan")
+        else:
+            case = _build(seed=312, ctx_lens=[3000, 1700, 257], G=2, Hg=4, d_idx=64, k=3,
+                          paged=True, poison="nan")
+        a = pu.gpu_path(case)
+        host = msa_synth.Case(**{**case.__dict__,
+                                 "k_cache": case.k_cache.cpu().pin_memory(),
+                                 "v_cache": case.v_cache.cpu().pin_memory()})
+        assert host.k_cache.is_pinned() and not host.k_cache.is_cuda
+        b = pu.gpu_path(host)
+        for key in a:
+            assert torch.equal(a[key], b[key]), key
+
+
+def test_host_cache_must_be_pinned():
+    """A pageable host cache is refused before anything is launched."""
+    import block_sparse_attention_09_amd as msa
+    case = _build(seed=313, ctx_lens=[600], G=1, Hg=4, d_idx=64, k=2, poison=False)
+    d = pu.dims_of(case)
+    sel = msa.msa_topk_blocks(d, msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table,
+                                                     case.row_pos, case.nb), case.row_pos, case.k)
+    pt = msa.msa_build_page_table(d, sel, case.block_table)
+    with pytest.raises(TypeError):
+        msa.msa_sparse_attn_decode(d, case.q, case.k_cache.cpu(), case.v_cache.cpu(), sel, pt,
+                                   case.row_pos)
+
+
 def test_merge_matches_oracle_merge():
     """The merge alone: oracle merge of exactly the bf16/fp32 partials the GPU merges."""
     import block_sparse_attention_09_amd as msa
