@@ -53,6 +53,7 @@ _SIGS = {
     "msa_sparse_attn_prefill": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
                                 ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
     "msa_lse_merge": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P],
+    "msa_gather_pages": [_DIMS, _I32, _P, _I32, View, View, _P, _P, _P, _P],
     "msa_peak_stream_read": [_P, ctypes.c_size_t, _P, _P],
     "msa_peak_mfma_bf16": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
 }
@@ -252,6 +253,33 @@ def msa_sparse_attn_prefill(dims: Dims, q, k_cache, v_cache, sel, page_table, ro
                                           _ptr(o_part), _ptr(lse_part), _stream(stream)),
            "msa_sparse_attn_prefill")
     return o_part, lse_part
+
+
+def msa_gather_pages(dims: Dims, page_table, k_cache, v_cache, dst_k=None, dst_v=None,
+                     dst_page_table=None, stream=None):
+    """Copy the pages a page table names (K and V, from device or pinned host
+    caches) into a compact device pool; returns (k_pool, v_pool, pool_page_table)
+    shaped so that msa_sparse_attn_decode can take them as its caches."""
+    _i32(page_table, "page_table")
+    rows, G, nslot = page_table.shape
+    units = rows * G * nslot
+    dev = page_table.device
+    if dst_k is None:
+        dst_k = torch.empty((units, 128, dims.D), dtype=torch.bfloat16, device=dev)
+    if dst_v is None:
+        dst_v = torch.empty((units, 128, dims.D), dtype=torch.bfloat16, device=dev)
+    if dst_page_table is None:
+        dst_page_table = torch.empty_like(page_table)
+    _need(dst_k, torch.bfloat16, "dst_k", True)
+    _need(dst_v, torch.bfloat16, "dst_v", True)
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_gather_pages(ctypes.byref(dims), rows, _ptr(page_table), nslot, kv[0], kv[1],
+                                   _ptr(dst_k), _ptr(dst_v), _ptr(dst_page_table),
+                                   _stream(stream)), "msa_gather_pages")
+    # one 128-token page per slot; the group is part of the slot, hence stride 0
+    k_pool = dst_k.view(units, 1, 128, dims.D).expand(units, G, 128, dims.D)
+    v_pool = dst_v.view(units, 1, 128, dims.D).expand(units, G, 128, dims.D)
+    return k_pool, v_pool, dst_page_table
 
 
 def msa_lse_merge(o_part, lse_part, o=None, lse=None, stream=None):

@@ -284,6 +284,28 @@ msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D, co
                       "msa_lse_merge");
 }
 
+msa_status_t msa_gather_pages(const msa_dims_t *dims, int32_t rows, const int32_t *page_table,
+                              int32_t nslot, msa_view_t k, msa_view_t v, void *dst_k,
+                              void *dst_v, int32_t *dst_page_table, msa_stream_t stream) {
+    msa_status_t st = check_dims(dims, false, true);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0 && nslot >= 1, MSA_ERR_INVALID, "rows >= 0 and nslot >= 1 are required");
+    if (rows == 0) return ok();
+    REQUIRE(page_table && dst_k && dst_v && dst_page_table, MSA_ERR_NULL,
+            "page_table, dst_k, dst_v and dst_page_table are required");
+    if ((st = check_view(k, "k")) != MSA_OK) return st;
+    if ((st = check_view(v, "v")) != MSA_OK) return st;
+    REQUIRE(aligned(dst_k, 16) && aligned(dst_v, 16), MSA_ERR_INVALID,
+            "dst_k and dst_v must be 16-byte aligned");
+    REQUIRE((int64_t)rows * dims->G * nslot < (int64_t)INT32_MAX, MSA_ERR_INVALID,
+            "rows * G * nslot must fit in int32 (the pool's page ids)");
+    return hip_status(msa::launch_gather_pages(rows, dims->G, nslot, page_table, k, v,
+                                               static_cast<msa::bf16_t *>(dst_k),
+                                               static_cast<msa::bf16_t *>(dst_v), dst_page_table,
+                                               as_stream(stream)),
+                      "msa_gather_pages");
+}
+
 msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
                                   msa_stream_t stream) {
     REQUIRE(bytes % 16 == 0, MSA_ERR_INVALID, "bytes = %zu must be a multiple of 16", bytes);

@@ -130,6 +130,11 @@ hipError_t launch_attn_prefill(const AttnArgs &a, int num_pages, void *workspace
 hipError_t launch_lse_merge(int rows, int H, int nslot, const bf16_t *o_part,
                             const float *lse_part, bf16_t *o, float *lse, hipStream_t stream);
 
+// copy of the selected K/V pages into a compact device pool (decoupled offload)
+hipError_t launch_gather_pages(int rows, int G, int nslot, const int32_t *page_table,
+                               const msa_view_t &k, const msa_view_t &v, bf16_t *dst_k,
+                               bf16_t *dst_v, int32_t *dst_page_table, hipStream_t stream);
+
 // measured-peak probes (not part of the MSA path)
 hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
                                    hipStream_t stream);

@@ -190,6 +190,29 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const 
                                     const int32_t *row_pos, float sm_scale, void *o_part,
                                     float *lse_part, msa_stream_t stream);
 
+/* ------------------------------------------------------------------ f4
+ * msa_gather_pages -- on-demand load of the selected KV pages.
+ * Pages: future-work section (未来工作) of the aihot.news page: the CPU offload
+ * of the key index and of the KV cache can be separated, the full key index
+ * loaded and the KV cache loaded on demand from the top-k selection.
+ *
+ * For u = (r*G + g)*nslot + s and p = page_table[r][g][s] >= 0, copies the 128
+ * tokens of page p, group g of k and of v (views, dim = D; typically pinned
+ * host memory, see msa_view_t) to dst_k[u] and dst_v[u], and writes
+ * dst_page_table[r][g][s] = u (-1 where p < 0).  msa_sparse_attn_decode then
+ * reads the pool through the views {dst_k or dst_v, page_stride = 128*D,
+ * group_stride = 0, token_stride = D} with dst_page_table, at device-memory
+ * speed; the copy reads whole 256-byte token rows.
+ *
+ *   page_table      int32 [rows][G][nslot]
+ *   dst_k, dst_v    device bf16 [rows*G*nslot][128][D], 16-byte aligned
+ *   dst_page_table  device int32 [rows][G][nslot]
+ * Errors: MSA_ERR_NULL, MSA_ERR_INVALID (alignment, sizes), MSA_ERR_UNSUPPORTED
+ * (D != 128), MSA_ERR_HIP. */
+msa_status_t msa_gather_pages(const msa_dims_t *dims, int32_t rows, const int32_t *page_table,
+                              int32_t nslot, msa_view_t k, msa_view_t v, void *dst_k,
+                              void *dst_v, int32_t *dst_page_table, msa_stream_t stream);
+
 /* ------------------------------------------------------------------ a8 / a9
  * msa_sparse_attn_prefill -- KV-block-major sparse attention.
  * Pages: KV-block-major section (KV 块主序稀疏注意力): many queries select the

@@ -161,6 +161,21 @@ def test_merge_validation(lib):
     assert lib.msa_lse_merge(0, 8, 3, 128, None, None, None, None, None) == MSA_OK
 
 
+def test_gather_pages_validation(lib):
+    d = _dims()
+    assert lib.msa_gather_pages(ctypes.byref(d), 0, None, 17, _view(), _view(), None, None, None,
+                                None) == MSA_OK
+    assert lib.msa_gather_pages(ctypes.byref(d), 4, None, 17, _view(), _view(), FAKE, FAKE, FAKE,
+                                None) == MSA_ERR_NULL
+    assert lib.msa_gather_pages(ctypes.byref(d), 4, FAKE, 0, _view(), _view(), FAKE, FAKE, FAKE,
+                                None) == MSA_ERR_INVALID
+    assert lib.msa_gather_pages(ctypes.byref(d), 4, FAKE, 17, _view(), _view(), MISALIGNED, FAKE,
+                                FAKE, None) == MSA_ERR_INVALID
+    d64 = _dims(D=64)
+    assert lib.msa_gather_pages(ctypes.byref(d64), 4, FAKE, 17, _view(), _view(), FAKE, FAKE,
+                                FAKE, None) == MSA_ERR_UNSUPPORTED
+
+
 def test_peak_probe_validation(lib):
     flops = ctypes.c_double(0.0)
     assert lib.msa_peak_stream_read(FAKE, 24, FAKE, None) == MSA_ERR_INVALID

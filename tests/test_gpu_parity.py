@@ -280,6 +280,36 @@ def test_kv_cache_in_pinned_host_memory():
             assert torch.equal(a[key], b[key]), key
 
 
+def test_gather_pages_then_decode():
+    """On-demand load: gathering the selected pages (from pinned host memory or
+    from the device cache) into a compact pool and running decode attention on
+    the pool gives the same partials, bit for bit, as decode on the cache."""
+    import block_sparse_attention_09_amd as msa
+    print("[case] gather pages then decode", flush=True)
+    case = _build(seed=314, ctx_lens=[3000, 1700, 257, 130], G=2, Hg=8, d_idx=128, k=3,
+                  paged=True, poison="nan")
+    d = pu.dims_of(case)
+    scale = 1.0 / math.sqrt(case.D)
+    scores = msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos,
+                                 case.nb, row_req=case.row_req)
+    sel, pt = msa.msa_topk_blocks_paged(d, scores, case.row_pos, case.k, case.block_table,
+                                        row_req=case.row_req)
+    ref = msa.msa_sparse_attn_decode(d, case.q, case.k_cache, case.v_cache, sel, pt,
+                                     case.row_pos, scale)
+    for where in ("device", "host"):
+        kc, vc = case.k_cache, case.v_cache
+        if where == "host":
+            kc, vc = kc.cpu().pin_memory(), vc.cpu().pin_memory()
+        kp, vp, ppt = msa.msa_gather_pages(d, pt, kc, vc)
+        out = msa.msa_sparse_attn_decode(d, case.q, kp, vp, sel, ppt, case.row_pos, scale)
+        torch.cuda.synchronize()
+        ptc, pptc = pt.cpu(), ppt.cpu()
+        assert torch.equal(pptc < 0, ptc < 0), where
+        units = torch.arange(ptc.numel(), dtype=torch.int32).view_as(ptc)
+        assert torch.equal(pptc[ptc >= 0], units[ptc >= 0]), where
+        assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1]), where
+
+
 def test_host_cache_must_be_pinned():
     """A pageable host cache is refused before anything is launched."""
     import block_sparse_attention_09_amd as msa
