@@ -10,6 +10,9 @@
  * over only those blocks.  The six compute calls below are the steps of that
  * path: index scoring, top-k block selection, page-table build, sparse decode
  * attention, KV-block-major sparse prefill attention and the log-sum-exp merge.
+ * Two more serve it: msa_topk_blocks_paged (selection and page table in one
+ * launch) and msa_gather_pages (the selected KV pages of a cache in host
+ * memory, loaded on demand into a device pool).
  *
  * Conventions shared by every call
  * --------------------------------
