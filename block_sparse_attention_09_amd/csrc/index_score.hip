@@ -280,7 +280,9 @@ hipError_t launch_index_score(const msa_dims_t &d, int rows, const bf16_t *q_idx
         return launch_index_score_tiled(d, rows, q_idx, kv, block_table, bt_stride, row_req,
                                         row_pos, blk_lo, scores, score_stride, stream);
     // One wave per resident wave slot of the device (the balanced kernel is
-    // meant to run in a single round), but no more than one per 4 blocks.
+    // meant to run in a single round), but no more than one per block: a small
+    // batch (a short context) then has every block's loads in flight at once
+    // instead of a few waves walking several blocks one after another.
     static std::atomic<int> resident_waves[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -300,7 +302,7 @@ hipError_t launch_index_score(const msa_dims_t &d, int rows, const bf16_t *q_idx
     const int64_t pairs = (int64_t)rows * d.G;
     const int64_t ub = pairs * score_stride;  // scored blocks, upper bound
     const int nwaves = (int)std::max<int64_t>(
-        1, std::min<int64_t>(resident_waves[dev].load(std::memory_order_relaxed), (ub + 3) / 4));
+        1, std::min<int64_t>(resident_waves[dev].load(std::memory_order_relaxed), ub));
     const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
     if (d.d_idx == 128)
         hipLaunchKernelGGL(index_score_stream_kernel<128>, grid, block, 0, stream, rows, d.G,
