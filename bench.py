@@ -2,9 +2,14 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workloads 2,5,3,4,1]
 
-A step is one pass of the whole path over one batch: index scores, top-k with
-the page table (msa_topk_blocks_paged: one kernel writes both), sparse attention
-(decode kernel, or the KV-block-major prefill), LSE merge.  The headline line is
+A step is one pass of the whole path over one batch: index scores, top-k, the
+page table, sparse attention (decode kernel, or the KV-block-major prefill), LSE
+merge.  Decode with the caches in device memory runs top-k, page table and
+decode attention as one call (msa_sparse_attn_decode_select, one kernel up to
+1,024 blocks per row when the batch fits one round of the GPU); prefill and the run with K/V in host memory call
+msa_topk_blocks_paged (one kernel for top-k and page table) and then the
+attention.  Every decode workload is also timed as the four separate calls, for
+the per-call figures.  The headline line is
 the decode workload at 64K context, batch 8 (8 KV groups x 8 heads, d_idx 128,
 top-16 + own block, paged): value = decode tokens/s of one MSA layer
 = batch x steps / time.  Each timed step starts from cold caches (an untimed
@@ -157,6 +162,34 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
         msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
         mark()
 
+    # Decode with the caches in device memory: the step that is timed and graphed
+    # runs selection, page table and decode attention as one call
+    # (msa_sparse_attn_decode_select); the four-call step above is timed first
+    # for the per-call breakdown.
+    fused = not case.prefill and not gather
+    fused_names = ["index_score", "select_attn", "merge"]
+
+    def step_fused(ev=None):
+        i = 0
+
+        def mark():
+            nonlocal i
+            if ev is not None:
+                ev[i].record()
+            i += 1
+        mark()
+        msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos, case.nb,
+                            row_req=case.row_req, blk_lo=case.blk_lo, num_reqs=case.num_reqs,
+                            scores=scores)
+        mark()
+        msa.msa_sparse_attn_decode_select(d, scores, case.k, case.block_table, case.q,
+                                          case.k_cache, case.v_cache, case.row_pos,
+                                          row_req=case.row_req, sm_scale=scale, sel=sel,
+                                          page_table=pt, o_part=o_part, lse_part=lse_part)
+        mark()
+        msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
+        mark()
+
     # Every timed step starts from cold caches: an untimed read of 1 GiB (four
     # times the 256 MB MALL) runs before it, so a step never finds the previous
     # step's K/V blocks or partials in L2/MALL (consecutive steps of one layer
@@ -187,11 +220,32 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     eager_ms = sum(step_ms)
     pct = {q: step_ms[min(steps - 1, int(round(q / 100 * (steps - 1))))] for q in (10, 50, 90)}
     o_ref, lse_ref = o.clone(), lse.clone()
+    sel_ref = sel.clone()
     alg = algorithmic(case, sel)
+    per_fused = None
+    if fused:
+        for _ in range(warmup):
+            step_fused()
+        torch.cuda.synchronize()
+        if not (torch.equal(o, o_ref) and torch.equal(lse, lse_ref) and torch.equal(sel, sel_ref)):
+            raise RuntimeError(f"{case.name}: the fused step differs from the four-call step")
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fused_names) + 1)]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush()
+            step_fused(fev[i])
+        torch.cuda.synchronize()
+        per_fused = {n: sum(fev[i][j].elapsed_time(fev[i][j + 1]) for i in range(steps)) / steps
+                     for j, n in enumerate(fused_names)}
+        step_ms = sorted(fev[i][0].elapsed_time(fev[i][len(fused_names)]) for i in range(steps))
+        eager_ms = sum(step_ms)
+        pct = {q: step_ms[min(steps - 1, int(round(q / 100 * (steps - 1))))] for q in (10, 50, 90)}
+        step = step_fused
     if not graph_replay:
         return case, dict(total_ms=eager_ms, ms_per_step=eager_ms / steps, eager_ms=eager_ms,
                           eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
-                          step_pct_ms=pct, alg=alg, sel=sel.cpu())
+                          per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu())
 
     # The same step captured once in a HIP graph and replayed: removes the
     # host launch gaps between the calls.  Every replay must reproduce the
@@ -234,7 +288,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     warm_ms = w0.elapsed_time(w1)
     return case, dict(total_ms=graph_ms, ms_per_step=graph_ms / steps, eager_ms=eager_ms,
                       eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
-                      step_pct_ms=pct, alg=alg, sel=sel.cpu(),
+                      per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu(),
                       warm_ms_per_step=warm_ms / steps)
 
 
@@ -323,6 +377,10 @@ def summarize(cfg, case, r, peaks=None):
                eager_ms_per_step=round(r["eager_ms_per_step"], 4),
                eager_step_ms_p10_p50_p90=[round(r["step_pct_ms"][q], 4) for q in (10, 50, 90)],
                per_call_us={k: round(v * 1e3, 2) for k, v in t.items()})
+    if r.get("per_call_fused_ms"):
+        res["step_calls"] = "index_score, select_attn (msa_sparse_attn_decode_select), merge"
+        res["fused_step_per_call_us"] = {k: round(v * 1e3, 2)
+                                         for k, v in r["per_call_fused_ms"].items()}
     if "warm_ms_per_step" in r:
         res["warm_cache_ms_per_step"] = round(r["warm_ms_per_step"], 4)
     if not case.prefill:
@@ -432,8 +490,11 @@ def main():
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(main_run["ms_per_step"], 4),
-        launch=("eager four-call step" if args.eager_only else
-                "hip graph replay of the four-call step (eager ms_per_step also reported)"),
+        launch=("eager step" if args.eager_only else
+                "hip graph replay of the step (eager ms_per_step also reported)"),
+        step=("three calls: msa_index_score, msa_sparse_attn_decode_select (top-k, page "
+              "table and decode attention in one launch), msa_lse_merge; per_call_us in the "
+              "workload entry times the same path as four calls"),
         timing=("sum over the steps of one HIP event pair around each step; an untimed "
                 "1 GiB read before every step leaves L2 and MALL cold"),
         warm_cache_ms_per_step=m.get("warm_cache_ms_per_step"),

@@ -8,7 +8,8 @@ the first call raises.
 
 Calls (same names and meaning as the C functions):
     msa_index_score, msa_topk_blocks, msa_build_page_table, msa_topk_blocks_paged,
-    msa_sparse_attn_decode, msa_prefill_workspace_size, msa_sparse_attn_prefill,
+    msa_sparse_attn_decode, msa_sparse_attn_decode_select, msa_prefill_workspace_size,
+    msa_sparse_attn_prefill,
     msa_lse_merge, msa_version, msa_gather_pages
 Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
     msa_peak_stream_read, msa_peak_mfma_bf16
@@ -27,6 +28,7 @@ from .binding import (  # noqa: F401
     msa_peak_stream_read,
     msa_prefill_workspace_size,
     msa_sparse_attn_decode,
+    msa_sparse_attn_decode_select,
     msa_sparse_attn_prefill,
     msa_topk_blocks,
     msa_topk_blocks_paged,

@@ -49,6 +49,8 @@ _SIGS = {
     "msa_build_page_table": [_DIMS, _I32, _P, _I32, _P, _P, _I32, _P, _P],
     "msa_sparse_attn_decode": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, ctypes.c_float,
                                _P, _P, _P],
+    "msa_sparse_attn_decode_select": [_DIMS, _I32, _P, _I32, _I32, _P, _P, _I32, _P, View, View,
+                                      _P, ctypes.c_float, _P, _P, _P, _P, _P],
     "msa_prefill_workspace_size": [_DIMS, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
     "msa_sparse_attn_prefill": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
                                 ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
@@ -225,6 +227,31 @@ def msa_sparse_attn_decode(dims: Dims, q, k_cache, v_cache, sel, page_table, row
                                          _ptr(o_part), _ptr(lse_part), _stream(stream)),
            "msa_sparse_attn_decode")
     return o_part, lse_part
+
+
+def msa_sparse_attn_decode_select(dims: Dims, scores, k, block_table, q, k_cache, v_cache,
+                                  row_pos, row_req=None, sm_scale=None, sel=None,
+                                  page_table=None, o_part=None, lse_part=None, stream=None):
+    """msa_topk_blocks_paged and msa_sparse_attn_decode in one launch; returns
+    (sel, page_table, o_part, lse_part)."""
+    _need(scores, torch.float32, "scores", True)
+    _need(q, torch.bfloat16, "q", True)
+    _i32(row_pos, "row_pos"), _i32(block_table, "block_table"), _i32(row_req, "row_req")
+    rows, _, score_stride = scores.shape
+    if sel is None:
+        sel = torch.empty((rows, dims.G, k + 1), dtype=torch.int32, device=scores.device)
+    if page_table is None:
+        page_table = torch.empty_like(sel)
+    _i32(sel, "sel"), _i32(page_table, "page_table")
+    o_part, lse_part = _attn_out(q, k + 1, o_part, lse_part)
+    scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dims.D))
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_sparse_attn_decode_select(
+        ctypes.byref(dims), rows, _ptr(scores), score_stride, k, _ptr(row_req),
+        _ptr(block_table), block_table.shape[1], _ptr(q), kv[0], kv[1], _ptr(row_pos), scale,
+        _ptr(sel), _ptr(page_table), _ptr(o_part), _ptr(lse_part), _stream(stream)),
+        "msa_sparse_attn_decode_select")
+    return sel, page_table, o_part, lse_part
 
 
 def msa_prefill_workspace_size(dims: Dims, rows, nslot, num_pages) -> int:

@@ -30,8 +30,10 @@
 // Decode: one workgroup per (row, group, slot), the block split over its four
 // waves (see attn_decode_kernel below).
 #include "msa_internal.h"
+#include "topk_select.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace msa {
 
@@ -554,10 +556,12 @@ __device__ __forceinline__ v4i16 lds_read_tr(const char *lds_byte_addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_byte_addr));
 }
 
+// Partial of one (row, group, slot) unit over block blk, cache page `page`,
+// with the workgroup's 32 KB of LDS; an empty slot (blk < 0) or a block wholly
+// past the row's position leaves an empty partial.
 template <int HG>
-__global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void attn_decode_kernel(
-    AttnArgs a, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
+__device__ __forceinline__ void decode_unit(const AttnArgs &a, char *lds, int unit, int blk,
+                                            int64_t page, float scale_log2) {
     using C = DecComb<HG>;
     // maxima and sums of wave i: ml(i)[0 .. 15] and ml(i)[16 .. 31]
     float *ml_extra = nullptr;
@@ -571,11 +575,9 @@ __global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void
         else
             return ml_extra + 32 * i;
     };
-    const int unit = blockIdx.x;  // (r, g, s)
-    const int s = unit % a.nslot;
+    const int s = unit % a.nslot;  // unit = (r, g, s)
     const int rg = unit / a.nslot;
     const int g = rg % a.G, r = rg / a.G;
-    const int blk = a.sel[unit];
     const int pos = a.row_pos[r];
     const int vis = pos - blk * kBlk;  // last visible token of the block
     if (blk < 0 || vis < 0) {
@@ -590,7 +592,6 @@ __global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void
     char *wl_base = lds + w * kWaveLds;
 
     if (w < nact) {
-        const int64_t page = a.page_table[unit];
         const int tok0 = w * kSlice;
         const bf16_t *kp = a.k + page * a.kps + (int64_t)g * a.kgs;
         const bf16_t *vp = a.v + page * a.vps + (int64_t)g * a.vgs;
@@ -722,6 +723,75 @@ __global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void
     }
 }
 
+template <int HG>
+__global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void attn_decode_kernel(
+    AttnArgs a, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
+    const int unit = blockIdx.x;
+    // the slot's block and page in one round trip (page -1 for an empty slot)
+    const int blk = a.sel[unit];
+    const int64_t page = a.page_table[unit];
+    decode_unit<HG>(a, lds, unit, blk, page, scale_log2);
+}
+
+// Selection + page table + decode attention in one launch: every workgroup of a
+// (row, group) runs the same top-k over the row's scores (exact integer
+// decisions, so all of them agree), keeps its own slot's block, writes that
+// slot of the selection and of the page table, and attends to it.  Wave 0
+// selects (no workgroup barrier inside the selection) while the other waves
+// wait; the block table entries of its candidates are read together with their
+// scores, so the selected page is known as soon as the block is.  The
+// selection's scratch lives in the LDS that the V slices use afterwards.
+template <int HG, int KPT>
+__global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void
+attn_decode_select_kernel(AttnArgs a, SelectArgs sa, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
+    using TS = TopkShared<1>;
+    static_assert(sizeof(TS) + 2 * sizeof(int) <= 4 * kWaveLds, "selection scratch");
+    const int unit = blockIdx.x;
+    const int s = unit % a.nslot, rg = unit / a.nslot, r = rg / a.G;
+    TS &sh = *reinterpret_cast<TS *>(lds);
+    int *pick = reinterpret_cast<int *>(lds + sizeof(TS));
+    if (threadIdx.x < kWave) {
+        const int own = a.row_pos[r] / kBlk;
+        const int req = sa.row_req ? sa.row_req[r] : r;
+        const int32_t *bt = sa.block_table + (int64_t)req * sa.bt_stride;
+        // block-table entries of the whole row, read with the scores (entries
+        // past the request's last block are never used)
+        const int n_bt = min(sa.score_stride, sa.bt_stride);
+        int pg[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int b = i * kWave + (int)threadIdx.x;
+            pg[i] = (b < n_bt) ? bt[b] : 0;
+        }
+        const int pg_own = bt[own];  // in flight while the selection runs
+        topk_select_regs<kWave, KPT>(
+            sa.scores + (int64_t)rg * sa.score_stride, sa.score_stride, own, sa.k, sh,
+            [&](int slot, int b, int i) {
+                if (slot == s) {
+                    int p = -1;
+                    if (b >= 0) {
+                        p = pg_own;
+#pragma unroll
+                        for (int j = 0; j < KPT; ++j) p = (j == i) ? pg[j] : p;
+                    }
+                    pick[0] = b;
+                    pick[1] = p;
+                }
+            });
+    }
+    __syncthreads();
+    const int blk = pick[0];
+    const int64_t page = pick[1];
+    if (threadIdx.x == 0) {
+        sa.sel[unit] = blk;
+        sa.page_table[unit] = (int32_t)page;
+    }
+    __syncthreads();  // the attention below reuses the selection's LDS
+    decode_unit<HG>(a, lds, unit, blk, page, scale_log2);
+}
+
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream) {
@@ -734,6 +804,49 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream) {
         case 8: hipLaunchKernelGGL(attn_decode_kernel<8>, grid, block, 0, stream, a, sl2); break;
         default: hipLaunchKernelGGL(attn_decode_kernel<16>, grid, block, 0, stream, a, sl2); break;
     }
+    return hipGetLastError();
+}
+
+template <int KPT>
+static void launch_decode_select_kpt(const AttnArgs &a, const SelectArgs &sa, float sl2,
+                                     dim3 grid, dim3 block, hipStream_t stream) {
+    switch (a.Hg) {
+        case 1: hipLaunchKernelGGL((attn_decode_select_kernel<1, KPT>), grid, block, 0, stream, a, sa, sl2); break;
+        case 2: hipLaunchKernelGGL((attn_decode_select_kernel<2, KPT>), grid, block, 0, stream, a, sa, sl2); break;
+        case 4: hipLaunchKernelGGL((attn_decode_select_kernel<4, KPT>), grid, block, 0, stream, a, sa, sl2); break;
+        case 8: hipLaunchKernelGGL((attn_decode_select_kernel<8, KPT>), grid, block, 0, stream, a, sa, sl2); break;
+        default: hipLaunchKernelGGL((attn_decode_select_kernel<16, KPT>), grid, block, 0, stream, a, sa, sl2); break;
+    }
+}
+
+// Workgroups of the fused kernel the device holds at once (one round), per
+// device; the kernels of every (Hg, KPT) use the same LDS and fit the same count.
+int decode_select_capacity() {
+    static std::atomic<int> cap[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev < 0 || dev >= 64) dev = 0;
+    int c = cap[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_decode_select_kernel<8, 16>,
+                                                         kDecThreads, 0) != hipSuccess)
+            return 0;
+        c = std::max(1, cus * per_cu);
+        cap[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+hipError_t launch_attn_decode_select(const AttnArgs &a, const SelectArgs &sa,
+                                     hipStream_t stream) {
+    if (sa.score_stride > kSelectMaxBlocks) return hipErrorInvalidValue;
+    const float sl2 = a.sm_scale * kLog2e;
+    const dim3 grid((unsigned)((int64_t)a.rows * a.G * a.nslot)), block(kDecThreads);
+    // scores per lane of the selecting wave
+    if (sa.score_stride <= 8 * kWave) launch_decode_select_kpt<8>(a, sa, sl2, grid, block, stream);
+    else launch_decode_select_kpt<16>(a, sa, sl2, grid, block, stream);
     return hipGetLastError();
 }
 

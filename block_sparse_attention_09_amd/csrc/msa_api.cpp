@@ -234,6 +234,41 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const 
     return hip_status(msa::launch_attn_decode(a, as_stream(stream)), "msa_sparse_attn_decode");
 }
 
+msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
+                                           const float *scores, int32_t score_stride, int32_t k,
+                                           const int32_t *row_req, const int32_t *block_table,
+                                           int32_t bt_stride, const void *q, msa_view_t kc,
+                                           msa_view_t vc, const int32_t *row_pos, float sm_scale,
+                                           int32_t *sel, int32_t *page_table, void *o_part,
+                                           float *lse_part, msa_stream_t stream) {
+    REQUIRE(k >= 0 && k < (1 << 30), MSA_ERR_INVALID, "k = %d must be >= 0", k);
+    REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
+    REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
+    const int32_t nslot = k + 1;
+    msa_status_t st = check_attn(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
+                                 sm_scale, o_part, lse_part);
+    if (st != MSA_OK) return st;
+    if (rows == 0) return ok();
+    REQUIRE(scores && block_table, MSA_ERR_NULL, "scores and block_table are required");
+    const msa::AttnArgs a = attn_args(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
+                                      sm_scale, o_part, lse_part);
+    // One kernel when its grid runs in a single round: every workgroup repeats
+    // its group's top-k, which costs nothing extra while all of them run at once
+    // but would be paid again by every later round of a larger batch.
+    const int64_t units = (int64_t)rows * dims->G * nslot;
+    if (score_stride <= msa::kSelectMaxBlocks && units <= msa::decode_select_capacity()) {
+        const msa::SelectArgs sa{scores, score_stride, k,   row_req,
+                                 block_table, bt_stride, sel, page_table};
+        return hip_status(msa::launch_attn_decode_select(a, sa, as_stream(stream)),
+                          "msa_sparse_attn_decode_select");
+    }
+    hipError_t e = msa::launch_topk(rows, dims->G, scores, score_stride, row_pos, k, sel,
+                                    as_stream(stream), row_req, block_table, bt_stride,
+                                    page_table);
+    if (e == hipSuccess) e = msa::launch_attn_decode(a, as_stream(stream));
+    return hip_status(e, "msa_sparse_attn_decode_select");
+}
+
 msa_status_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t rows, int32_t nslot,
                                         int32_t num_pages, size_t *bytes) {
     REQUIRE(bytes, MSA_ERR_NULL, "bytes is NULL");

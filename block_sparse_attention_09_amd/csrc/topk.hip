@@ -19,6 +19,7 @@
 // index) and the rest is padded with -1.  Integer decisions on the caller's
 // fp32 scores only, so the result is exact and deterministic.
 #include "msa_internal.h"
+#include "topk_select.h"
 
 namespace msa {
 
@@ -27,15 +28,6 @@ namespace {
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 
-// Order-preserving key: larger float -> larger unsigned; -0 and +0 map together.
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (f == 0.0f) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix count of `flag` over the workgroup in thread order; returns
-// the prefix for this thread and writes the workgroup total to *total.
 // Optional page-table output written next to the selection: page of slot i =
 // block_table[request][sel[i]], -1 for an empty slot.  With pt == nullptr the
 // top-k kernels write the selection only.
@@ -63,209 +55,25 @@ struct PageOut {
     }
 };
 
-template <int NWAVES = kTopkWaves>
-__device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int *total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint64_t bal = __ballot(flag);
-    const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    if (NWAVES == 1) {
-        *total = __popcll(bal);
-        return in_wave;
-    }
-    if (lane == 0) wave_tot[w] = __popcll(bal);
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NWAVES; ++i) {
-        const int c = wave_tot[i];
-        before += (i < w) ? c : 0;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return before + in_wave;
-}
-
-// Workgroup minimum and maximum of the valid (non-zero) keys: *lo = ~0u and
-// *hi = 0 when there are none.  `xch` holds 2 * NWAVES words of LDS.
-template <int NWAVES>
-__device__ __forceinline__ void key_range(uint32_t lo, uint32_t hi, uint32_t *xch,
-                                          uint32_t *lo_out, uint32_t *hi_out) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
-    }
-    if (NWAVES > 1) {
-        const int w = threadIdx.x >> 6;
-        if ((threadIdx.x & 63) == 0) {
-            xch[2 * w] = lo;
-            xch[2 * w + 1] = hi;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NWAVES; ++i) {
-            lo = min(lo, xch[2 * i]);
-            hi = max(hi, xch[2 * i + 1]);
-        }
-        __syncthreads();
-    }
-    *lo_out = lo;
-    *hi_out = hi;
-}
-
-// First digit shift of the radix select: the 8 bits that start at the highest
-// bit where the smallest and largest candidate keys differ (the bits above it
-// are common to every candidate and carry no rank information).  -1 when every
-// candidate key is the same.
-__device__ __forceinline__ int first_shift(uint32_t lo, uint32_t hi) {
-    const uint32_t diff = lo ^ hi;
-    if (diff == 0u) return -1;
-    const int top = 31 - __clz((int)diff);
-    return top > 7 ? top - 7 : 0;
-}
-
-// Digit d of the current radix pass such that the keys above it number fewer
-// than `remain` and those at or above it at least `remain`; one wave scans the
-// 256-bin histogram (4 bins per lane, suffix sums from the top digit down).
-__device__ __forceinline__ void find_digit(const uint32_t *hist, int remain, int *digit,
-                                           int *above_out) {
-    const int lane = threadIdx.x & 63;
-    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const int local = (int)(h0 + h1 + h2 + h3);
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int v = __shfl_down(incl, off, kWave);
-        incl += (lane + off < kWave) ? v : 0;
-    }
-    int above = incl - local;  // keys in digits owned by higher lanes
-    const int hd[4] = {(int)h0, (int)h1, (int)h2, (int)h3};
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-        if (above < remain && remain <= above + hd[e]) {
-            *digit = 4 * lane + e;
-            *above_out = above;
-        }
-        above += hd[e];
-    }
-}
-
-// Register-resident variant: the scores of one (row, group) are read once into
-// KPT keys per thread (block b = i * THREADS + tid, so loads are coalesced and
-// the ordered pass walks b in ascending order); the radix passes then run on
-// registers with an LDS histogram.  THREADS = 64 needs no workgroup barrier
-// beyond the single wave's own.
+// Register-resident variant: one workgroup per (row, group) holds its scores in
+// registers (topk_select_regs); THREADS = 64 needs no workgroup barrier beyond
+// the single wave's own.
 template <int THREADS, int KPT>
 __global__ __launch_bounds__(THREADS) void topk_reg_kernel(int G, const float *__restrict__ scores,
                                                            int score_stride,
                                                            const int32_t *__restrict__ row_pos,
                                                            int k, int32_t *__restrict__ sel,
                                                            PageOut po) {
-    constexpr int NW = THREADS / kWave;
-    __shared__ uint32_t hist[256];
-    __shared__ int wave_tot[NW];
-    __shared__ uint32_t range_xch[2 * NW];
-    __shared__ int sh_digit, sh_above;
+    __shared__ TopkShared<THREADS / kWave> sh;
     const int rg = blockIdx.x;
-    const int tid = threadIdx.x;
     const int own = row_pos[rg / G] / kBlk;
-    const float *s = scores + (int64_t)rg * score_stride;
     int32_t *out = sel + (int64_t)rg * (k + 1);
     const PageRow pr = po.row(rg, G, k);
-
-    // key 0 marks "not a candidate"; every finite score's key is > 0
-    uint32_t key[KPT];
-    int nvalid = 0;
-    uint32_t klo = ~0u, khi = 0u;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int b = i * THREADS + tid;
-        const float v = (b < own) ? s[b] : -INFINITY;
-        key[i] = (v != -INFINITY) ? order_key(v) : 0u;
-        nvalid += key[i] != 0u;
-        klo = (key[i] != 0u) ? min(klo, key[i]) : klo;
-        khi = max(khi, key[i]);
-    }
-    int ncand;
-    {
-        // workgroup sum of nvalid
-        int x = nvalid;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
-        if (NW == 1) {
-            ncand = x;
-        } else {
-            if ((tid & 63) == 0) wave_tot[tid >> 6] = x;
-            __syncthreads();
-            ncand = 0;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) ncand += wave_tot[i];
-            __syncthreads();
-        }
-    }
-
-    // keep keys whose top bits (tmask) exceed thresh, plus the first take_eq
-    // (in block order) whose top bits equal it
-    uint32_t thresh = 0u, tmask = 0xffffffffu;
-    int take_eq = 0;
-    if (k == 0) {
-        thresh = 0xffffffffu;
-    } else if (k < ncand) {
-        uint32_t lo, hi;
-        key_range<NW>(klo, khi, range_xch, &lo, &hi);
-        uint32_t prefix = 0u, pmask = 0u;
-        int remain = k;
-        // digit passes from the highest differing bit down, 8 bits at a time; the
-        // last one may overlap bits already fixed, which all counted keys share
-        for (int shift = first_shift(lo, hi); shift >= 0; shift = shift > 8 ? shift - 8 : 0) {
-            for (int i = tid; i < 256; i += THREADS) hist[i] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < KPT; ++i)
-                if (key[i] != 0u && (key[i] & pmask) == prefix)
-                    atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
-            __syncthreads();
-            if (tid < kWave) find_digit(hist, remain, &sh_digit, &sh_above);
-            __syncthreads();
-            prefix |= (uint32_t)sh_digit << shift;
-            pmask |= 255u << shift;
-            remain -= sh_above;
-            const bool whole_bucket = (int)hist[sh_digit] == remain;
-            __syncthreads();
-            if (whole_bucket || shift == 0) break;  // selection decided
-        }
-        thresh = prefix;
-        tmask = pmask;
-        take_eq = remain;
-    }
-
-    int n_sel = 0, n_eq = 0;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        if (i * THREADS >= own) break;  // uniform
-        const int b = i * THREADS + tid;
-        const bool valid = key[i] != 0u;
-        const uint32_t kk = key[i] & tmask;
-        const bool is_eq = valid && kk == thresh && take_eq > 0;
-        int eq_tot;
-        const int eq_rank = n_eq + block_excl_count<NW>(is_eq, wave_tot, &eq_tot);
-        const bool keep = valid && (kk > thresh || (is_eq && eq_rank < take_eq));
-        int keep_tot;
-        const int at = n_sel + block_excl_count<NW>(keep, wave_tot, &keep_tot);
-        if (keep) {
-            out[at] = b;
-            pr.put(at, b);
-        }
-        n_sel += keep_tot;
-        n_eq += eq_tot;
-    }
-    for (int i = n_sel + tid; i <= k; i += THREADS) {
-        const int b = (i == n_sel) ? own : -1;
-        out[i] = b;
-        pr.put(i, b);
-    }
+    topk_select_regs<THREADS, KPT>(scores + (int64_t)rg * score_stride, score_stride, own, k, sh,
+                                   [&](int slot, int b, int) {
+                                       out[slot] = b;
+                                       pr.put(slot, b);
+                                   });
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int G, const float *__restrict__ scores,

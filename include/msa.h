@@ -10,9 +10,10 @@
  * over only those blocks.  The six compute calls below are the steps of that
  * path: index scoring, top-k block selection, page-table build, sparse decode
  * attention, KV-block-major sparse prefill attention and the log-sum-exp merge.
- * Two more serve it: msa_topk_blocks_paged (selection and page table in one
- * launch) and msa_gather_pages (the selected KV pages of a cache in host
- * memory, loaded on demand into a device pool).
+ * Three more serve it: msa_topk_blocks_paged (selection and page table in one
+ * launch), msa_sparse_attn_decode_select (selection, page table and decode
+ * attention in one launch) and msa_gather_pages (the selected KV pages of a
+ * cache in host memory, loaded on demand into a device pool).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -192,6 +193,30 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const 
                                     const int32_t *page_table, int32_t nslot,
                                     const int32_t *row_pos, float sm_scale, void *o_part,
                                     float *lse_part, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ a2 + a3 + a4
+ * msa_sparse_attn_decode_select -- msa_topk_blocks_paged and
+ * msa_sparse_attn_decode in one launch.  Pages: the new smaller kernels of the
+ * path, the top-k among them, are named as fusion candidates (未来工作); the
+ * selection feeds the paged decode attention (将 MSA 与分页注意力集成).
+ *
+ * Writes exactly what msa_topk_blocks_paged (sel, page_table; nslot = k + 1)
+ * followed by msa_sparse_attn_decode (o_part, lse_part) write, bit for bit.
+ * With score_stride <= 1024 and rows * G * (k + 1) workgroups that the device
+ * holds at once (one round; 1,280 on MI355X) it is one kernel: each workgroup
+ * of a (row, group) repeats that group's top-k over its scores (integer
+ * decisions, so every copy agrees) and attends to its own slot, so the decode
+ * step loses one launch and the wait between the two kernels.  Otherwise
+ * (longer score rows, or a batch whose later rounds would pay the repeated
+ * top-k again) it runs the two kernels one after the other.  Arguments as in those two calls (sel and
+ * page_table are outputs here; row_req may be NULL). */
+msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
+                                           const float *scores, int32_t score_stride, int32_t k,
+                                           const int32_t *row_req, const int32_t *block_table,
+                                           int32_t bt_stride, const void *q, msa_view_t kc,
+                                           msa_view_t vc, const int32_t *row_pos, float sm_scale,
+                                           int32_t *sel, int32_t *page_table, void *o_part,
+                                           float *lse_part, msa_stream_t stream);
 
 /* ------------------------------------------------------------------ f4
  * msa_gather_pages -- on-demand load of the selected KV pages.

@@ -57,6 +57,18 @@ def gpu_path(case, prefill=None, sel=None, pt=None, sm_scale=None):
     else:
         o_part, lse_part = msa.msa_sparse_attn_decode(d, case.q, case.k_cache, case.v_cache,
                                                       use_sel, use_pt, case.row_pos, scale)
+        if sel is None and pt is None:
+            # the fused selection + page table + decode attention call writes the
+            # same four arrays, bit for bit
+            sel_d, pt_d, o_d, lse_d = msa.msa_sparse_attn_decode_select(
+                d, scores, case.k, case.block_table, case.q, case.k_cache, case.v_cache,
+                case.row_pos, row_req=case.row_req, sm_scale=scale)
+            assert torch.equal(sel_d, sel_gpu), "msa_sparse_attn_decode_select: sel differs"
+            assert torch.equal(pt_d, pt_gpu), "msa_sparse_attn_decode_select: page table differs"
+            assert torch.equal(o_d.view(torch.int16), o_part.view(torch.int16)), \
+                "msa_sparse_attn_decode_select: o_part differs"
+            assert torch.equal(lse_d.view(torch.int32), lse_part.view(torch.int32)), \
+                "msa_sparse_attn_decode_select: lse_part differs"
     o, lse = msa.msa_lse_merge(o_part, lse_part)
     torch.cuda.synchronize()
     return {k: v.cpu() for k, v in dict(scores=scores, sel=sel_gpu, pt=pt_gpu, o_part=o_part,

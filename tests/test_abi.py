@@ -134,6 +134,30 @@ def test_attention_validation(lib):
     assert _decode(lib, _dims(), rows=0) == MSA_OK
 
 
+def _decode_select(lib, dims, **kw):
+    a = dict(rows=1, scores=FAKE, ss=4, k=2, rr=None, bt=FAKE, bts=4, q=FAKE, kc=_view(),
+             vc=_view(), rp=FAKE, scale=0.088, sel=FAKE, pt=FAKE, o=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.msa_sparse_attn_decode_select(
+        ctypes.byref(dims), a["rows"], a["scores"], a["ss"], a["k"], a["rr"], a["bt"], a["bts"],
+        a["q"], a["kc"], a["vc"], a["rp"], a["scale"], a["sel"], a["pt"], a["o"], a["lse"], None)
+
+
+def test_decode_select_validation(lib):
+    assert _decode_select(lib, _dims(D=64)) == MSA_ERR_UNSUPPORTED
+    assert _decode_select(lib, _dims(), k=-1) == MSA_ERR_INVALID
+    assert _decode_select(lib, _dims(), ss=0) == MSA_ERR_INVALID
+    assert _decode_select(lib, _dims(), bts=0) == MSA_ERR_INVALID
+    assert _decode_select(lib, _dims(), scale=0.0) == MSA_ERR_INVALID
+    assert _decode_select(lib, _dims(), o=MISALIGNED) == MSA_ERR_INVALID
+    assert _decode_select(lib, _dims(), scores=None) == MSA_ERR_NULL
+    assert _decode_select(lib, _dims(), bt=None) == MSA_ERR_NULL
+    assert _decode_select(lib, _dims(), sel=None) == MSA_ERR_NULL
+    assert _decode_select(lib, _dims(), pt=None) == MSA_ERR_NULL
+    assert _decode_select(lib, _dims(), rows=0, scores=None, bt=None, q=None, sel=None, pt=None,
+                          rp=None, o=None, lse=None) == MSA_OK
+
+
 def test_prefill_workspace(lib):
     d = _dims()
     n = ctypes.c_size_t(0)

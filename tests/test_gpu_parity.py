@@ -41,6 +41,10 @@ SMALL = {
     # lower bounds drawn up to 1.5x the block count: some groups score only their own block
     "lo-above-own": dict(seed=109, ctx_lens=[900, 1400, 2000], G=2, Hg=4, d_idx=64, k=3,
                          lo_frac=1.5),
+    # long score rows in a small batch: 782 blocks per row (the one-kernel selection +
+    # decode attention with 16 scores per lane), 1,954 (past its limit: two kernels)
+    "long-782": dict(seed=111, ctx_lens=[100_000, 65_000], G=2, Hg=4, d_idx=64, k=8),
+    "long-1954": dict(seed=112, ctx_lens=[250_000, 131_073], G=2, Hg=4, d_idx=64, k=16),
     # 3,000 (row, group) pairs of 3 blocks: more pairs than the scan has waves, so
     # waves fill several pairs' -inf ranges and slices cross many pair boundaries
     "many-pairs": dict(seed=110, ctx_lens=[300 + (i % 7) * 13 for i in range(1000)], G=3, Hg=2,
