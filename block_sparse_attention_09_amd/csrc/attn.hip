@@ -402,11 +402,13 @@ __global__ void remap_scatter_kernel(AttnArgs a, int32_t *__restrict__ cursor,
 // Multi-workgroup counting sort (used while the G * P units fit an LDS
 // histogram): workgroup w takes a contiguous chunk of the flattened (row,
 // group, slot) selection, counts it per unit in LDS and writes its counts to
-// column w of cnt[unit][W]; a wave per unit turns each row of cnt into an
+// row w of cnt[W][unit]; 16 threads per unit turn its column of cnt into an
 // exclusive prefix over the workgroups (and the unit's total), the
 // single-workgroup scan turns the totals into list offsets, and each workgroup
-// places its chunk again with LDS cursors.  No global atomics: the atomic
-// inversion costs two contended global atomics per entry.
+// places its chunk again with LDS cursors that start at offs[u] + cnt[w][u],
+// so an entry's place in the list is one LDS atomic away.  Every global access
+// of the three passes is coalesced, and there are no global atomics (the
+// atomic inversion costs two contended global atomics per entry).
 constexpr int kRemapThreads = 1024;
 constexpr int kRemapMaxUnits = 16384;  // LDS histogram of 64 KB
 
@@ -437,37 +439,52 @@ __global__ __launch_bounds__(kRemapThreads) void remap_hist_kernel(AttnArgs a, i
         atomicAdd(&hist[a.page_table[i] * a.G + g], 1);
     }
     __syncthreads();
-    for (int u = threadIdx.x; u < units; u += kRemapThreads) cnt[(int64_t)u * W + w] = hist[u];
+    for (int u = threadIdx.x; u < units; u += kRemapThreads) cnt[(int64_t)w * units + u] = hist[u];
 }
 
-__global__ void remap_unitscan_kernel(int units, int W, int32_t *__restrict__ cnt,
-                                      int32_t *__restrict__ total) {
-    const int lane = threadIdx.x & 63;
-    const int u = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
-    if (u >= units) return;  // whole waves leave together
-    int32_t *c = cnt + (int64_t)u * W;
-    int run = 0;
-    for (int w0 = 0; w0 < W; w0 += kWave) {
-        const int x = (w0 + lane < W) ? c[w0 + lane] : 0;
-        int incl = x;
+// Exclusive prefix over the workgroups of every unit's column of cnt[W][unit],
+// in place, and the unit totals: 16 units per workgroup and 16 threads per
+// unit, each thread a run of up to 16 workgroup rows with all its loads in
+// flight at once; the runs' sums are combined in LDS.  Needs W <= 256.
+__global__ __launch_bounds__(256) void remap_unitscan_kernel(int units, int W,
+                                                             int32_t *__restrict__ cnt,
+                                                             int32_t *__restrict__ total) {
+    __shared__ int part_sum[16][16];
+    const int ul = threadIdx.x & 15, part = threadIdx.x >> 4;
+    const int u = blockIdx.x * 16 + ul;
+    const int rp = (W + 15) / 16;  // rows per run
+    const int w0 = part * rp;
+    int x[16];
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int v = __shfl_up(incl, off, kWave);
-            incl += (lane >= off) ? v : 0;
-        }
-        if (w0 + lane < W) c[w0 + lane] = run + incl - x;
-        run += __shfl(incl, kWave - 1, kWave);
+    for (int i = 0; i < 16; ++i)
+        x[i] = (u < units && i < rp && w0 + i < W) ? cnt[(int64_t)(w0 + i) * units + u] : 0;
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int v = x[i];
+        x[i] = run;
+        run += v;
     }
-    if (lane == 0) total[u] = run;
+    part_sum[part][ul] = run;
+    __syncthreads();
+    int base = 0;
+    for (int q = 0; q < part; ++q) base += part_sum[q][ul];
+    if (u < units) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (i < rp && w0 + i < W) cnt[(int64_t)(w0 + i) * units + u] = base + x[i];
+        if (part == 15) total[u] = base + run;
+    }
 }
 
 __global__ __launch_bounds__(kRemapThreads) void remap_place_kernel(
     AttnArgs a, int units, int W, int64_t chunk, const int32_t *__restrict__ cnt,
     const int32_t *__restrict__ offs, int32_t *__restrict__ list) {
     __shared__ int32_t cur[kRemapMaxUnits];
-    for (int u = threadIdx.x; u < units; u += kRemapThreads) cur[u] = 0;
-    __syncthreads();
     const int w = blockIdx.x;
+    for (int u = threadIdx.x; u < units; u += kRemapThreads)
+        cur[u] = offs[u] + cnt[(int64_t)w * units + u];
+    __syncthreads();
     const int64_t n = (int64_t)a.rows * a.G * a.nslot;
     const int64_t i1 = min(n, (w + 1) * chunk);
     for (int64_t i = w * chunk + threadIdx.x; i < i1; i += kRemapThreads) {
@@ -475,8 +492,7 @@ __global__ __launch_bounds__(kRemapThreads) void remap_place_kernel(
         int r, g, s;
         remap_entry(a, i, r, g, s);
         const int u = a.page_table[i] * a.G + g;
-        const int at = atomicAdd(&cur[u], 1);
-        list[offs[u] + cnt[(int64_t)u * W + w] + at] = r * a.nslot + s;
+        list[atomicAdd(&cur[u], 1)] = r * a.nslot + s;
     }
 }
 
@@ -852,12 +868,13 @@ hipError_t launch_attn_decode_select(const AttnArgs &a, const SelectArgs &sa,
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workgroups of the counting sort: enough that each chunk is a few times the
-// unit count, at most 256; 0 selects the atomic inversion (units beyond the
-// LDS histogram).
+// Workgroups of the counting sort: about one selection entry per unit and
+// workgroup (each workgroup also clears, writes and reads back one count per
+// unit), at most 256 (one per CU); 0 selects the atomic inversion (units
+// beyond the LDS histogram).
 static int remap_workgroups(int64_t n, int64_t units) {
     if (units > kRemapMaxUnits) return 0;
-    const int64_t w = n / (4 * units + 1) + 1;
+    const int64_t w = n / (units + 1) + 1;
     return (int)std::min<int64_t>(256, w);
 }
 
@@ -894,8 +911,8 @@ hipError_t launch_attn_prefill(const AttnArgs &a, int P, void *workspace, hipStr
     if (W > 0) {
         const int64_t chunk = (n + W - 1) / W;
         MSA_BY_HG(remap_hist_kernel, dim3(W), dim3(kRemapThreads), a, (int)units, W, chunk, cnt)
-        hipLaunchKernelGGL(remap_unitscan_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0,
-                           stream, (int)units, W, cnt, counts);
+        hipLaunchKernelGGL(remap_unitscan_kernel, dim3((unsigned)((units + 15) / 16)), dim3(256),
+                           0, stream, (int)units, W, cnt, counts);
         hipLaunchKernelGGL(remap_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts,
                            offs, (int)units);
         hipLaunchKernelGGL(remap_place_kernel, dim3(W), dim3(kRemapThreads), 0, stream, a,
