@@ -357,12 +357,14 @@ def test_empty_rows_is_noop():
     assert s.shape == (0, 2, case.nb)
 
 
-@pytest.mark.parametrize("prefill", [False, True])
-def test_graph_replay_matches_eager(prefill):
-    """The five-call step captured in a HIP graph: every replay (with eager work
-    and synchronisations in between) equals the eager result bit for bit."""
+@pytest.mark.parametrize("form", ["decode", "decode-select", "prefill"])
+def test_graph_replay_matches_eager(form):
+    """The step captured in a HIP graph (five calls, or three with the fused
+    select + decode attention): every replay (with eager work and
+    synchronisations in between) equals the eager result bit for bit."""
     import block_sparse_attention_09_amd as msa
-    print(f"[case] graph replay prefill={prefill}", flush=True)
+    prefill = form == "prefill"
+    print(f"[case] graph replay {form}", flush=True)
     if prefill:
         case = _build(seed=501, ctx_lens=[2500], G=2, Hg=8, d_idx=128, k=3, prefill_rows=400)
     else:
@@ -382,6 +384,13 @@ def test_graph_replay_matches_eager(prefill):
     def step():
         msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos, case.nb,
                             row_req=case.row_req, num_reqs=case.num_reqs, scores=scores)
+        if form == "decode-select":
+            msa.msa_sparse_attn_decode_select(d, scores, case.k, case.block_table, case.q,
+                                              case.k_cache, case.v_cache, case.row_pos,
+                                              row_req=case.row_req, sel=sel, page_table=pt,
+                                              o_part=o_part, lse_part=lse_part)
+            msa.msa_lse_merge(o_part, lse_part, o=o, lse=lse)
+            return
         msa.msa_topk_blocks(d, scores, case.row_pos, case.k, sel=sel)
         msa.msa_build_page_table(d, sel, case.block_table, row_req=case.row_req, page_table=pt)
         if prefill:
@@ -409,6 +418,8 @@ def test_graph_replay_matches_eager(prefill):
         for t in (scores, o_part, o):
             t.zero_()
         sel.fill_(-7)
+        pt.fill_(-7)
+        lse_part.fill_(1.0)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
