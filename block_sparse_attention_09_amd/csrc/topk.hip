@@ -202,7 +202,12 @@ hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
 #define MSA_TOPK_REG(T, K)                                                                  \
     hipLaunchKernelGGL((topk_reg_kernel<T, K>), grid, dim3(T), 0, stream, G, scores,        \
                        score_stride, row_pos, k, sel, po)
+    // (one wave: as many scores per lane as the row needs, so that no lane
+    // converts, counts and ranks empty register slots)
     if (score_stride <= 64 * 8) MSA_TOPK_REG(64, 8);
+    else if (score_stride <= 64 * 9) MSA_TOPK_REG(64, 9);
+    else if (score_stride <= 64 * 10) MSA_TOPK_REG(64, 10);
+    else if (score_stride <= 64 * 12) MSA_TOPK_REG(64, 12);
     else if (score_stride <= 64 * 16) MSA_TOPK_REG(64, 16);
     else if (score_stride <= 256 * 16) MSA_TOPK_REG(256, 16);
     else if (score_stride <= 256 * 32) MSA_TOPK_REG(256, 32);
