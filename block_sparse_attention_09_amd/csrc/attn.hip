@@ -836,21 +836,27 @@ static void launch_decode_select_kpt(const AttnArgs &a, const SelectArgs &sa, fl
 }
 
 // Workgroups of the fused kernel the device holds at once (one round), per
-// device; the kernels of every (Hg, KPT) use the same LDS and fit the same count.
-int decode_select_capacity() {
-    static std::atomic<int> cap[64];
+// device: the kernels of Hg <= 8 share one occupancy (LDS-bound), Hg = 16 keeps
+// its maxima and sums in a separate LDS array and fits fewer.
+int decode_select_capacity(int Hg) {
+    static std::atomic<int> cap[64][2];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev < 0 || dev >= 64) dev = 0;
-    int c = cap[dev].load(std::memory_order_relaxed);
+    const int v = Hg > 8 ? 1 : 0;
+    int c = cap[dev][v].load(std::memory_order_relaxed);
     if (c == 0) {
         int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_decode_select_kernel<8, 16>,
-                                                         kDecThreads, 0) != hipSuccess)
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
+        const hipError_t e =
+            v ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, attn_decode_select_kernel<16, 16>, kDecThreads, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, attn_decode_select_kernel<8, 16>, kDecThreads, 0);
+        if (e != hipSuccess) return 0;
         c = std::max(1, cus * per_cu);
-        cap[dev].store(c, std::memory_order_relaxed);
+        cap[dev][v].store(c, std::memory_order_relaxed);
     }
     return c;
 }

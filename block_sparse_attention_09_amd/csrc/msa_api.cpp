@@ -256,7 +256,7 @@ msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
     // its group's top-k, which costs nothing extra while all of them run at once
     // but would be paid again by every later round of a larger batch.
     const int64_t units = (int64_t)rows * dims->G * nslot;
-    if (score_stride <= msa::kSelectMaxBlocks && units <= msa::decode_select_capacity()) {
+    if (score_stride <= msa::kSelectMaxBlocks && units <= msa::decode_select_capacity(dims->Hg)) {
         const msa::SelectArgs sa{scores, score_stride, k,   row_req,
                                  block_table, bt_stride, sel, page_table};
         return hip_status(msa::launch_attn_decode_select(a, sa, as_stream(stream)),

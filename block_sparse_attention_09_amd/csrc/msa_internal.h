@@ -125,7 +125,7 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
 
 // Top-k + page table + decode attention in one launch (sel, page_table written
 // by the kernel; a.sel / a.page_table unused).  Scores per (row, group) at most
-// kSelectMaxBlocks.  decode_select_capacity() is the number of its workgroups
+// kSelectMaxBlocks.  decode_select_capacity(Hg) is the number of its workgroups
 // the device holds at once (0 if the query fails).
 struct SelectArgs {
     const float *scores;
@@ -136,7 +136,7 @@ struct SelectArgs {
 };
 constexpr int kSelectMaxBlocks = 1024;
 hipError_t launch_attn_decode_select(const AttnArgs &a, const SelectArgs &sa, hipStream_t stream);
-int decode_select_capacity();
+int decode_select_capacity(int Hg);
 
 size_t prefill_workspace_bytes(int rows, int G, int nslot, int num_pages);
 hipError_t launch_attn_prefill(const AttnArgs &a, int num_pages, void *workspace,
