@@ -112,7 +112,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     pt = torch.empty_like(sel)
     o_part = torch.empty((case.rows, case.H, case.nslot, case.D), dtype=torch.bfloat16,
                          device=dev)
-    lse_part = torch.empty((case.rows, case.H, case.nslot), dtype=torch.float32, device=dev)
+    lse_part = msa.empty_lse_part(case.rows, case.H, case.nslot, dev)
     o = torch.empty((case.rows, case.H, case.D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((case.rows, case.H), dtype=torch.float32, device=dev)
     ws = None

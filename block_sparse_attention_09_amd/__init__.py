@@ -11,6 +11,7 @@ Calls (same names and meaning as the C functions):
     msa_sparse_attn_decode, msa_sparse_attn_decode_select, msa_prefill_workspace_size,
     msa_sparse_attn_prefill,
     msa_lse_merge, msa_version, msa_gather_pages
+Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout)
 Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
     msa_peak_stream_read, msa_peak_mfma_bf16
 """
@@ -18,6 +19,7 @@ from .binding import (  # noqa: F401
     Dims,
     MSAError,
     View,
+    empty_lse_part,
     lib_path,
     load,
     msa_build_page_table,

@@ -205,12 +205,31 @@ def msa_build_page_table(dims: Dims, sel, block_table, row_req=None, page_table=
     return page_table
 
 
+def empty_lse_part(rows, H, nslot, device) -> torch.Tensor:
+    """Partial LSEs as the C ABI lays them out, [rows][nslot][H] in memory,
+    returned as the view indexed [row][head][slot] (the order of o_part)."""
+    return torch.empty((rows, nslot, H), dtype=torch.float32, device=device).permute(0, 2, 1)
+
+
+def _need_lse(lse_part, shape=None):
+    """lse_part must be a float32 device view [rows][H][nslot] over memory laid
+    out [rows][nslot][H] (as empty_lse_part makes it)."""
+    if lse_part.dtype != torch.float32 or not lse_part.is_cuda:
+        raise TypeError("lse_part: expected a float32 device tensor")
+    if lse_part.dim() != 3 or not lse_part.permute(0, 2, 1).is_contiguous():
+        raise ValueError("lse_part must be a [rows][H][nslot] view of [rows][nslot][H] memory "
+                         "(see empty_lse_part)")
+    if shape is not None and tuple(lse_part.shape) != tuple(shape):
+        raise ValueError(f"lse_part: shape {tuple(lse_part.shape)}, expected {tuple(shape)}")
+
+
 def _attn_out(q, nslot, o_part, lse_part):
     rows, H, D = q.shape
     if o_part is None:
         o_part = torch.empty((rows, H, nslot, D), dtype=torch.bfloat16, device=q.device)
     if lse_part is None:
-        lse_part = torch.empty((rows, H, nslot), dtype=torch.float32, device=q.device)
+        lse_part = empty_lse_part(rows, H, nslot, q.device)
+    _need_lse(lse_part, (rows, H, nslot))
     return o_part, lse_part
 
 
@@ -311,8 +330,8 @@ def msa_gather_pages(dims: Dims, page_table, k_cache, v_cache, dst_k=None, dst_v
 
 def msa_lse_merge(o_part, lse_part, o=None, lse=None, stream=None):
     _need(o_part, torch.bfloat16, "o_part", True)
-    _need(lse_part, torch.float32, "lse_part", True)
     rows, H, nslot, D = o_part.shape
+    _need_lse(lse_part, (rows, H, nslot))
     if o is None:
         o = torch.empty((rows, H, D), dtype=torch.bfloat16, device=o_part.device)
     if lse is None:

@@ -104,6 +104,13 @@ __device__ __forceinline__ void stage_kv_store(AttnSmem &sm, const KvStage &st, 
     }
 }
 
+// Index of the LSE of (row r, slot s, head h) in lse_part [rows][nslot][H]:
+// the heads of one (row, slot) are contiguous, so the Hg LSEs a (row, group,
+// slot) produces land in one sector instead of Hg scattered ones.
+__device__ __forceinline__ int64_t lse_index(const AttnArgs &a, int r, int s, int h) {
+    return ((int64_t)r * a.nslot + s) * (a.G * a.Hg) + h;
+}
+
 // o = 0, lse = -inf for the Hg heads of an empty (row, group, slot).
 template <int HG>
 __device__ __forceinline__ void write_empty_slot(const AttnArgs &a, int r, int g, int s, int tid,
@@ -113,7 +120,7 @@ __device__ __forceinline__ void write_empty_slot(const AttnArgs &a, int r, int g
         const int hh = i >> 4, ch = i & 15;
         const int64_t oi = ((int64_t)r * H + g * HG + hh) * a.nslot + s;
         *reinterpret_cast<u32x4 *>(a.o_part + oi * 128 + ch * 8) = u32x4{0u, 0u, 0u, 0u};
-        if (ch == 0) a.lse_part[oi] = -INFINITY;
+        if (ch == 0) a.lse_part[lse_index(a, r, s, g * HG + hh)] = -INFINITY;
     }
 }
 
@@ -319,9 +326,12 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
                     }
                 }
             }
+            // the Hg heads of a query token: Hg consecutive LSEs (one 32-byte
+            // sector for Hg = 8) written by one instruction
             if (meta.valid && h == 0)
                 __builtin_nontemporal_store((mx * scale_log2 + __builtin_amdgcn_logf(l)) * kLn2,
-                                            a.lse_part + oi);
+                                            a.lse_part + lse_index(a, meta.row, meta.slot,
+                                                                   g * HG + hh));
         }
         meta = meta_next;
     }
@@ -735,7 +745,9 @@ __device__ __forceinline__ void decode_unit(const AttnArgs &a, char *lds, int un
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
         *reinterpret_cast<u32x4 *>(a.o_part + oi * 128 + 8 * c) = out;
-        if (c == 0) a.lse_part[oi] = (m * scale_log2 + __builtin_amdgcn_logf(L)) * kLn2;
+        if (c == 0)
+            a.lse_part[lse_index(a, r, s, g * HG + hh)] =
+                (m * scale_log2 + __builtin_amdgcn_logf(L)) * kLn2;
     }
 }
 

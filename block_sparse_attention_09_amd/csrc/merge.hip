@@ -9,7 +9,8 @@
 // Slots with lse = -inf (empty) are skipped.
 //
 // HBM-bound: 16 lanes own one (row, head) pair, 8 dims (16 B) each, so a wave
-// streams four pairs' partial rows with 16-byte loads.  Partials are read once:
+// streams four pairs' partial rows with 16-byte loads; the 32 pairs of a
+// workgroup are consecutive heads, whose LSEs for one slot are contiguous.  Partials are read once:
 // the loads are non-temporal (5 % faster on the prefill shape than cached ones),
 // and each LSE is loaded by one lane and shuffled to the others (a further 6 %).
 // The output rows are stored non-temporally too: on the prefill shape, right
@@ -24,8 +25,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// 16 lanes own one (row, head) pair, 8 dims (16 B) each; a 256-thread
-// workgroup serves 16 pairs.  Slots go in batches of kBatch (one batch holds a
+// 16 lanes own one (row, head) pair, 8 dims (16 B) each; a workgroup of
+// THREADS threads serves THREADS / 16 pairs, consecutive heads.  Large merges
+// (prefill) take 512 threads, so that the 32 heads' LSEs of one slot fill one
+// 128-byte line; small ones (decode) 256, for twice the workgroups.  Slots go in batches of kBatch (one batch holds a
 // top-16 + own selection) with every load of a batch -- the batch's LSEs and
 // all its partial rows -- issued before any is used, so a pair costs one
 // memory round trip per batch; batches are combined with a running maximum.
@@ -33,17 +36,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // select, so whatever that row holds never reaches the result.
 constexpr int kBatch = 17;
 static_assert(kBatch == 17, "the LSE hand-round covers 16 lanes plus one");
-constexpr int kMergeThreads = 256;
-
-__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(int64_t pairs, int nslot,
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void lse_merge_kernel(int64_t pairs, int H, int nslot,
                                                                   const bf16_t *__restrict__ o_part,
                                                                   const float *__restrict__ lse_part,
                                                                   bf16_t *__restrict__ o,
                                                                   float *__restrict__ lse) {
-    const int64_t pair = (int64_t)blockIdx.x * (kMergeThreads / 16) + (threadIdx.x >> 4);
+    const int64_t pair = (int64_t)blockIdx.x * (THREADS / 16) + (threadIdx.x >> 4);
     const int sub = threadIdx.x & 15;
     if (pair >= pairs) return;  // whole 16-lane groups leave together
-    const float *ls = lse_part + pair * nslot;
+    // this pair's LSEs: lse_part [rows][nslot][H], slot s at ls[s * H]
+    const int64_t row = pair / H;
+    const float *ls = lse_part + row * nslot * H + (pair - row * H);
     const bf16_t *op = o_part + pair * nslot * 128 + sub * 8;
     float m = -INFINITY, wsum = 0.f;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -52,9 +56,12 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(int64_t pairs,
         u32x4 v[kBatch];
         // the batch's LSEs: one load per lane (lane sub holds slot s0 + sub, lane
         // 0 also slot s0 + 16), handed round the 16 lanes of the pair
-        const float la = (s0 + sub < nslot) ? __builtin_nontemporal_load(ls + s0 + sub) : -INFINITY;
-        const float lb =
-            (sub == 0 && s0 + 16 < nslot) ? __builtin_nontemporal_load(ls + s0 + 16) : -INFINITY;
+        const float la = (s0 + sub < nslot)
+                             ? __builtin_nontemporal_load(ls + (int64_t)(s0 + sub) * H)
+                             : -INFINITY;
+        const float lb = (sub == 0 && s0 + 16 < nslot)
+                             ? __builtin_nontemporal_load(ls + (int64_t)(s0 + 16) * H)
+                             : -INFINITY;
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const bool in = s0 + i < nslot;
@@ -102,9 +109,13 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(int64_t pairs,
 hipError_t launch_lse_merge(int rows, int H, int nslot, const bf16_t *o_part,
                             const float *lse_part, bf16_t *o, float *lse, hipStream_t stream) {
     const int64_t pairs = (int64_t)rows * H;
-    const int64_t per_wg = kMergeThreads / 16;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((pairs + per_wg - 1) / per_wg)),
-                       dim3(kMergeThreads), 0, stream, pairs, nslot, o_part, lse_part, o, lse);
+    // 512 threads once the merge fills the device several times over
+    if (pairs >= (int64_t)1 << 16)
+        hipLaunchKernelGGL(lse_merge_kernel<512>, dim3((unsigned)((pairs + 31) / 32)), dim3(512),
+                           0, stream, pairs, H, nslot, o_part, lse_part, o, lse);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel<256>, dim3((unsigned)((pairs + 15) / 16)), dim3(256),
+                           0, stream, pairs, H, nslot, o_part, lse_part, o, lse);
     return hipGetLastError();
 }
 

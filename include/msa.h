@@ -180,13 +180,15 @@ msa_status_t msa_topk_blocks_paged(const msa_dims_t *dims, int32_t rows, const f
  * softmax attention of q[r][h] over the tokens t of page page_table[r][g][s]
  * with 128 b + t <= row_pos[r], logits scaled by sm_scale:
  *     o_part[r][h][s][:] = normalised output (bf16),
- *     lse_part[r][h][s]  = m + ln(sum exp(z - m)) in natural log (fp32).
+ *     lse_part[r][s][h]  = m + ln(sum exp(z - m)) in natural log (fp32).
  * Empty slots get o = 0 and lse = -inf.  Combine with msa_lse_merge.
  *
  *   q         bf16 [rows][G*Hg][D], contiguous, 16-byte aligned
  *   k, v      key / value cache views, dim = D
  *   sel, page_table  int32 [rows][G][nslot]
- *   o_part    bf16 [rows][G*Hg][nslot][D];  lse_part fp32 [rows][G*Hg][nslot]
+ *   o_part    bf16 [rows][G*Hg][nslot][D];  lse_part fp32 [rows][nslot][G*Hg]
+ *             (the LSEs of one (row, slot) are contiguous over the heads, so the
+ *             Hg heads of a (row, group, slot) share one 32-byte sector)
  * bf16 inputs, fp32 accumulation on the matrix cores. */
 msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const void *q,
                                     msa_view_t k, msa_view_t v, const int32_t *sel,
@@ -276,7 +278,7 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t rows, const
  * Slots with lse = -inf are skipped; a (row, head) with none gets o = 0 and
  * lse = -inf.
  *
- *   o_part  bf16 [rows][H][nslot][D];  lse_part fp32 [rows][H][nslot]
+ *   o_part  bf16 [rows][H][nslot][D];  lse_part fp32 [rows][nslot][H]
  *   o       bf16 [rows][H][D];         lse      fp32 [rows][H] (may be NULL)
  *   D must be 128. */
 msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D,

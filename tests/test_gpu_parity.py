@@ -328,20 +328,30 @@ def test_host_cache_must_be_pinned():
                                    case.row_pos)
 
 
-def test_merge_matches_oracle_merge():
-    """The merge alone: oracle merge of exactly the bf16/fp32 partials the GPU merges."""
+@pytest.mark.parametrize("rows,H,nslot", [(33, 8, 9), (1100, 64, 5), (5500, 12, 3)])
+def test_merge_matches_oracle_merge(rows, H, nslot):
+    """The merge alone: oracle merge of exactly the bf16/fp32 partials the GPU merges
+    (the two larger cases take the 512-thread workgroups, the last with workgroups
+    that straddle rows)."""
     import block_sparse_attention_09_amd as msa
-    print("[case] merge", flush=True)
-    g = torch.Generator(device="cpu").manual_seed(5)
-    rows, H, nslot = 33, 8, 9
+    print(f"[case] merge rows={rows} H={H} nslot={nslot}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(5 + rows)
     op = torch.randn((rows, H, nslot, 128), generator=g).to(torch.bfloat16)
     lp = (torch.randn((rows, H, nslot), generator=g) * 4).float()
-    lp[0, :, 3:] = -math.inf
+    lp[0, :, 2:] = -math.inf
     lp[1, 2, :] = -math.inf
     op[lp == -math.inf] = 0
-    o, lse = msa.msa_lse_merge(op.to(DEV), lp.to(DEV))
+    # partial LSEs in the C ABI's [rows][nslot][H] memory layout, viewed [row][head][slot]
+    lp_dev = msa.empty_lse_part(rows, H, nslot, DEV)
+    lp_dev.copy_(lp)
+    with pytest.raises(ValueError):
+        msa.msa_lse_merge(op.to(DEV), lp.to(DEV))  # [rows][H][nslot] memory: refused
+    o, lse = msa.msa_lse_merge(op.to(DEV), lp_dev)
     o_ref, lse_ref = oracle.lse_merge(op.double().numpy(), lp.double().numpy())
-    assert np.max(np.abs(o.float().cpu().numpy() - o_ref)) <= 8e-3
+    # the output is bf16: one rounding (at most half an ulp, <= 2^-8 relative) on
+    # top of the fp32 sums
+    err = np.abs(o.float().cpu().numpy() - o_ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(o_ref) + 1e-3), float(np.max(err))
     l = lse.cpu().numpy()
     assert np.isneginf(l[1, 2]) and bool(torch.all(o[1, 2].cpu() == 0))
     fin = ~np.isneginf(lse_ref)
@@ -376,7 +386,7 @@ def test_graph_replay_matches_eager(form):
     sel = torch.empty((case.rows, case.G, case.nslot), dtype=torch.int32, device=dev)
     pt = torch.empty_like(sel)
     o_part = torch.empty((case.rows, case.H, case.nslot, 128), dtype=torch.bfloat16, device=dev)
-    lse_part = torch.empty((case.rows, case.H, case.nslot), dtype=torch.float32, device=dev)
+    lse_part = msa.empty_lse_part(case.rows, case.H, case.nslot, dev)
     o = torch.empty((case.rows, case.H, 128), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((case.rows, case.H), dtype=torch.float32, device=dev)
     ws = torch.empty(msa.msa_prefill_workspace_size(d, case.rows, case.nslot, case.num_pages),
