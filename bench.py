@@ -222,6 +222,24 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     o_ref, lse_ref = o.clone(), lse.clone()
     sel_ref = sel.clone()
     alg = algorithmic(case, sel)
+    # The index-score kernel alone, launched back to back between one event
+    # pair after a cache flush: each dispatch overlaps the previous launch, so
+    # the average is the kernel's own duration (the per-launch event pairs above
+    # also hold the dispatch latency in front of the kernel).
+    score_btb_ms = None
+    if not case.prefill:
+        reps = 10
+        flush()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(reps):
+            msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos,
+                                case.nb, row_req=case.row_req, blk_lo=case.blk_lo,
+                                num_reqs=case.num_reqs, scores=scores)
+        b1.record()
+        torch.cuda.synchronize()
+        score_btb_ms = b0.elapsed_time(b1) / reps
     per_fused = None
     if fused:
         for _ in range(warmup):
@@ -245,7 +263,8 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     if not graph_replay:
         return case, dict(total_ms=eager_ms, ms_per_step=eager_ms / steps, eager_ms=eager_ms,
                           eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
-                          per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu())
+                          per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu(),
+                          score_btb_ms=score_btb_ms)
 
     # The same step captured once in a HIP graph and replayed: removes the
     # host launch gaps between the calls.  Every replay must reproduce the
@@ -289,7 +308,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     return case, dict(total_ms=graph_ms, ms_per_step=graph_ms / steps, eager_ms=eager_ms,
                       eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
                       per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu(),
-                      warm_ms_per_step=warm_ms / steps)
+                      warm_ms_per_step=warm_ms / steps, score_btb_ms=score_btb_ms)
 
 
 def traffic_from_profile():
@@ -390,6 +409,10 @@ def summarize(cfg, case, r, peaks=None):
         if peaks:
             res["index_score_frac_of_measured_read"] = round(
                 score_gbps / peaks["stream_read_GBps"], 4)
+        if r.get("score_btb_ms"):
+            res["index_score_back_to_back_us"] = round(r["score_btb_ms"] * 1e3, 2)
+            res["index_score_back_to_back_GBps"] = round(
+                a["score_bytes"] / (r["score_btb_ms"] * 1e-3) / 1e9, 1)
         res["index_scan_GBps"] = round((a["kidx"] + a["qidx"]) /
                                        ((t["index_score"] + t["topk_page_table"]) * 1e-3) / 1e9, 1)
     merge_bytes = a["part_bytes"] + a["qo_bytes"] // 2   # partials read, output written
@@ -482,6 +505,13 @@ def main():
                     traffic=traffic_from_profile(), alg_bytes_per_launch=a["score_bytes"],
                     avg_launch_us=round(t_score * 1e3, 2),
                     frac_of_measured_read=round(achieved / peaks["stream_read_GBps"], 4))
+    btb = main_run.get("score_btb_ms")
+    if btb:
+        # the same kernel timed back to back (see run_workload): its own duration,
+        # without the dispatch latency each per-launch event pair also holds
+        roofline["back_to_back_us"] = round(btb * 1e3, 2)
+        roofline["back_to_back_achieved"] = round(a["score_bytes"] / (btb * 1e-3) / 1e9, 1)
+        roofline["back_to_back_frac"] = round(roofline["back_to_back_achieved"] / HBM_PEAK_GBPS, 4)
     cpu = None
     if not args.no_cpu_baseline and main_case is not None and not main_case.prefill:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
