@@ -210,8 +210,10 @@ hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
     else if (score_stride <= 64 * 12) MSA_TOPK_REG(64, 12);
     else if (score_stride <= 64 * 16) MSA_TOPK_REG(64, 16);
     else if (score_stride <= 256 * 16) MSA_TOPK_REG(256, 16);
-    else if (score_stride <= 256 * 32) MSA_TOPK_REG(256, 32);
-    else if (score_stride <= 256 * 64) MSA_TOPK_REG(256, 64);
+    // long rows: more threads, fewer scores each (8,192 blocks: 28 -> 20 us
+    // against 256 threads x 32)
+    else if (score_stride <= 1024 * 8) MSA_TOPK_REG(1024, 8);
+    else if (score_stride <= 1024 * 16) MSA_TOPK_REG(1024, 16);
     else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, stream, G, scores,
                             score_stride, row_pos, k, sel, po);
 #undef MSA_TOPK_REG
