@@ -209,9 +209,10 @@ hipError_t launch_topk(int rows, int G, const float *scores, int score_stride,
     else if (score_stride <= 64 * 10) MSA_TOPK_REG(64, 10);
     else if (score_stride <= 64 * 12) MSA_TOPK_REG(64, 12);
     else if (score_stride <= 64 * 16) MSA_TOPK_REG(64, 16);
-    else if (score_stride <= 256 * 16) MSA_TOPK_REG(256, 16);
-    // long rows: more threads, fewer scores each (8,192 blocks: 28 -> 20 us
-    // against 256 threads x 32)
+    // longer rows: 1,024 threads, few scores each (2,048 blocks: 14 -> 11 us
+    // against 256 threads x 16; 8,192 blocks: 28 -> 20 us against 256 x 32)
+    else if (score_stride <= 1024 * 2) MSA_TOPK_REG(1024, 2);
+    else if (score_stride <= 1024 * 4) MSA_TOPK_REG(1024, 4);
     else if (score_stride <= 1024 * 8) MSA_TOPK_REG(1024, 8);
     else if (score_stride <= 1024 * 16) MSA_TOPK_REG(1024, 16);
     else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, stream, G, scores,

@@ -79,13 +79,13 @@ def test_small_decode_path(name):
     pu.check_output(res["o"], res["lse"], o, lse)
 
 
-@pytest.mark.parametrize("nb", [512, 560, 600, 700, 3000, 5000, 9000, 17000])
+@pytest.mark.parametrize("nb", [512, 560, 600, 700, 1500, 3000, 5000, 9000, 17000])
 def test_topk_exact_on_oracle_scores(nb):
     """Given identical fp32 scores the selection is integer work: bit-exact,
     including exact ties (scores drawn from a few levels) and -inf holes.  The
     block counts cover every kernel variant (one wave with 8, 9, 10, 12 or 16 keys
-    per lane, one workgroup with 16, 32 or 64 keys per thread, and the
-    global-memory fallback)."""
+    per lane, 1,024 threads with 2, 4, 8 or 16 keys each, and the global-memory
+    fallback)."""
     import block_sparse_attention_09_amd as msa
     print(f"[case] topk exact nb={nb}", flush=True)
     rng = np.random.default_rng(9 + nb)
