@@ -773,22 +773,23 @@ __global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void
 // Selection + page table + decode attention in one launch: every workgroup of a
 // (row, group) runs the same top-k over the row's scores (exact integer
 // decisions, so all of them agree), keeps its own slot's block, writes that
-// slot of the selection and of the page table, and attends to it.  Wave 0
-// selects (no workgroup barrier inside the selection) while the other waves
-// wait; the block table entries of its candidates are read together with their
-// scores, so the selected page is known as soon as the block is.  The
-// selection's scratch lives in the LDS that the V slices use afterwards.
+// slot of the selection and of the page table, and attends to it.  All four
+// waves select, KPT scores per thread (0.9 us faster on a 64K-context batch
+// than one wave with four times as many); the block-table entries of the
+// candidates are read together with their scores, so the selected page is
+// known as soon as the block is.  The selection's scratch lives in the LDS
+// that the V slices use afterwards.
 template <int HG, int KPT>
 __global__ __launch_bounds__(kDecThreads, DecComb<HG>::ml_in_slice ? 5 : 4) void
 attn_decode_select_kernel(AttnArgs a, SelectArgs sa, float scale_log2) {
     __shared__ __attribute__((aligned(16))) char lds[4 * kWaveLds];
-    using TS = TopkShared<1>;
+    using TS = TopkShared<kDecThreads / kWave>;
     static_assert(sizeof(TS) + 2 * sizeof(int) <= 4 * kWaveLds, "selection scratch");
     const int unit = blockIdx.x;
     const int s = unit % a.nslot, rg = unit / a.nslot, r = rg / a.G;
     TS &sh = *reinterpret_cast<TS *>(lds);
     int *pick = reinterpret_cast<int *>(lds + sizeof(TS));
-    if (threadIdx.x < kWave) {
+    {
         const int own = a.row_pos[r] / kBlk;
         const int req = sa.row_req ? sa.row_req[r] : r;
         const int32_t *bt = sa.block_table + (int64_t)req * sa.bt_stride;
@@ -798,11 +799,11 @@ attn_decode_select_kernel(AttnArgs a, SelectArgs sa, float scale_log2) {
         int pg[KPT];
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int b = i * kWave + (int)threadIdx.x;
+            const int b = i * kDecThreads + (int)threadIdx.x;
             pg[i] = (b < n_bt) ? bt[b] : 0;
         }
         const int pg_own = bt[own];  // in flight while the selection runs
-        topk_select_regs<kWave, KPT>(
+        topk_select_regs<kDecThreads, KPT>(
             sa.scores + (int64_t)rg * sa.score_stride, sa.score_stride, own, sa.k, sh,
             [&](int slot, int b, int i) {
                 if (slot == s) {
@@ -871,9 +872,9 @@ int decode_select_capacity(int Hg) {
             return 0;
         const hipError_t e =
             v ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, attn_decode_select_kernel<16, 16>, kDecThreads, 0)
+                    &per_cu, attn_decode_select_kernel<16, 4>, kDecThreads, 0)
               : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, attn_decode_select_kernel<8, 16>, kDecThreads, 0);
+                    &per_cu, attn_decode_select_kernel<8, 4>, kDecThreads, 0);
         if (e != hipSuccess) return 0;
         c = std::max(1, cus * per_cu);
         cap[dev][v].store(c, std::memory_order_relaxed);
@@ -886,9 +887,9 @@ hipError_t launch_attn_decode_select(const AttnArgs &a, const SelectArgs &sa,
     if (sa.score_stride > kSelectMaxBlocks) return hipErrorInvalidValue;
     const float sl2 = a.sm_scale * kLog2e;
     const dim3 grid((unsigned)((int64_t)a.rows * a.G * a.nslot)), block(kDecThreads);
-    // scores per lane of the selecting wave
-    if (sa.score_stride <= 8 * kWave) launch_decode_select_kpt<8>(a, sa, sl2, grid, block, stream);
-    else launch_decode_select_kpt<16>(a, sa, sl2, grid, block, stream);
+    // scores per thread of the selecting workgroup
+    if (sa.score_stride <= 2 * kDecThreads) launch_decode_select_kpt<2>(a, sa, sl2, grid, block, stream);
+    else launch_decode_select_kpt<4>(a, sa, sl2, grid, block, stream);
     return hipGetLastError();
 }
 
