@@ -45,6 +45,12 @@ SMALL = {
     # decode attention with 16 scores per lane), 1,954 (past its limit: two kernels)
     "long-782": dict(seed=111, ctx_lens=[100_000, 65_000], G=2, Hg=4, d_idx=64, k=8),
     "long-1954": dict(seed=112, ctx_lens=[250_000, 131_073], G=2, Hg=4, d_idx=64, k=16),
+    # either side of the select call's one-round rule (8 groups x 17 slots: 9 rows =
+    # 1,224 workgroups run as one kernel, 10 rows = 1,360 as two on a 256-CU part)
+    "one-round-9": dict(seed=113, ctx_lens=[3000 + 97 * i for i in range(9)], G=8, Hg=8,
+                        d_idx=128, k=16),
+    "one-round-10": dict(seed=114, ctx_lens=[3000 + 97 * i for i in range(10)], G=8, Hg=8,
+                         d_idx=128, k=16),
     # 3,000 (row, group) pairs of 3 blocks: more pairs than the scan has waves, so
     # waves fill several pairs' -inf ranges and slices cross many pair boundaries
     "many-pairs": dict(seed=110, ctx_lens=[300 + (i % 7) * 13 for i in range(1000)], G=3, Hg=2,
