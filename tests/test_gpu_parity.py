@@ -334,11 +334,11 @@ def test_host_cache_must_be_pinned():
                                    case.row_pos)
 
 
-@pytest.mark.parametrize("rows,H,nslot", [(33, 8, 9), (1100, 64, 5), (5500, 12, 3)])
+@pytest.mark.parametrize("rows,H,nslot", [(33, 8, 9), (1100, 64, 5), (5500, 12, 3), (1030, 64, 18)])
 def test_merge_matches_oracle_merge(rows, H, nslot):
     """The merge alone: oracle merge of exactly the bf16/fp32 partials the GPU merges
-    (the two larger cases take the 512-thread workgroups, the last with workgroups
-    that straddle rows)."""
+    (the three larger cases take the 512-thread workgroups: one with workgroups
+    that straddle rows, one with two batches of slots)."""
     import block_sparse_attention_09_amd as msa
     print(f"[case] merge rows={rows} H={H} nslot={nslot}", flush=True)
     g = torch.Generator(device="cpu").manual_seed(5 + rows)
