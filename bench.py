@@ -21,7 +21,8 @@ Also reported on the same line:
                 against 8 TB/s HBM, from HIP events around every launch in the
                 timed region; traffic from the committed rocprofv3 counter
                 summary when it was taken on the current kernel source
-  cpu_baseline  the CPU oracle on the host cores over the same batch
+  cpu_baseline  the CPU oracle on the host cores over the same batch (every
+                workload entry carries its own oracle timing, per stage)
   workloads     the other seeded workloads (1M-context decode, ragged decode,
                 prefill chunk, 4K latency case), each timed the same way
 """
@@ -324,31 +325,104 @@ def traffic_from_profile():
     return info.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case):
-    """The oracle, as it stands, on the host cores over the whole headline batch."""
-    import numpy as np
-    import msa_synth
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_NATIVE_ORACLE = None
+
+
+def _oracle_for_host():
+    """The oracle as it stands, compiled for this host's CPU (-O3 -march=native,
+    strict IEEE: the same results as the portable build the tests use)."""
+    global _NATIVE_ORACLE
     import oracle
-    bits = msa_synth.bits
-    args = dict(q_idx=bits(case.q_idx), k_idx=bits(case.k_idx), q=bits(case.q),
-                k_pool=bits(case.k_cache), v_pool=bits(case.v_cache))
-    bt = case.block_table.cpu().numpy()
-    pos = case.row_pos.cpu().numpy()
-    # repeat whole-batch passes until about 10 s of host work
-    t = time.perf_counter()
-    passes = 0
+    if _NATIVE_ORACLE is None:
+        _NATIVE_ORACLE = oracle.build_native(os.path.join(ROOT, "oracle", "_host"))
+        oracle.use_library(_NATIVE_ORACLE)
+    return oracle
+
+
+# rows of each workload the oracle is timed on: every row of the decode batches,
+# 256 evenly spaced rows of the 8,192-row prefill chunk (scaled to the chunk)
+CPU_MIN_SECONDS = {1: 2.0, 2: 10.0}     # repeat whole passes for at least this long
+PREFILL_CPU_ROWS = 256
+
+
+def cpu_oracle(cfg, case, alg):
+    """The oracle timed per stage on the host cores, on host copies of the same
+    inputs: index score, top-k, page table, per-block attention partials and the
+    LSE merge (the stages of the GPU path), each by perf_counter around its call.
+    Copies to the host are not timed.  Stage times are scaled to the whole batch
+    when only a sample of rows is timed."""
+    import numpy as np
+    from oracle import inputs
+    orc = _oracle_for_host()
+    if case.prefill:
+        rows = list(range(0, case.rows, max(1, case.rows // PREFILL_CPU_ROWS)))
+    else:
+        rows = list(range(case.rows))
+    scale_rows = case.rows / len(rows)
+    h = inputs.host_rows(case, rows)
+    bt_real = case.block_table.cpu().numpy()
+    rr_real = case.row_req.cpu().numpy()[rows]
+    sm = 1.0 / math.sqrt(case.D)
+    kv = {}
+
+    def one_pass():
+        t = [time.perf_counter()]
+        s = orc.index_score(h["q_idx"], h["k_idx"], h["bt"], h["row_pos"], case.nb,
+                            row_req=h["row_req"], blk_lo=h["blk_lo"])
+        t.append(time.perf_counter())
+        sel = orc.topk(s.astype(np.float32), h["row_pos"], case.k)
+        t.append(time.perf_counter())
+        orc.page_table(sel, h["bt"], h["row_req"])
+        t.append(time.perf_counter())
+        if "pools" not in kv:     # the K/V pages this selection names, copied once (untimed)
+            pt_real = orc.page_table(sel, bt_real, rr_real)
+            kv["pools"] = inputs.host_kv_pages(case, pt_real)
+        kp, vp, pt_c = kv["pools"]
+        t.append(time.perf_counter())
+        op, lp = orc.attn_partials(h["q"], kp, vp, sel, pt_c, h["row_pos"], sm)
+        t.append(time.perf_counter())
+        orc.lse_merge(op, lp)
+        t.append(time.perf_counter())
+        return [t[1] - t[0], t[2] - t[1], t[3] - t[2], t[5] - t[4], t[6] - t[5]]
+
+    runs = []
+    min_s = CPU_MIN_SECONDS.get(cfg, 0.0)
+    if min_s:
+        one_pass()                               # warm-up
+    t0 = time.perf_counter()
     while True:
-        oracle.decode_path(args["q_idx"], args["k_idx"], args["q"], args["k_pool"],
-                           args["v_pool"], bt, pos, case.k, case.nb, 1.0 / math.sqrt(case.D))
-        passes += 1
-        dt = time.perf_counter() - t
-        if dt >= 10.0 or passes >= 1000:
+        runs.append(one_pass())
+        if time.perf_counter() - t0 >= min_s or len(runs) >= 1000:
             break
-    return dict(value=case.rows * passes / dt, unit="tok/s", cores=oracle.num_threads(),
-                kind="oracle", seconds=round(dt, 3),
-                sample=f"{passes} passes over the whole {case.name} batch ({case.rows} requests "
-                       f"x {case.G} groups): index scores, top-k, page table, direct attention; "
-                       "fp64 C oracle")
+    med = [sorted(r[i] for r in runs)[len(runs) // 2] for i in range(5)]
+    names = ["index_score", "topk", "page_table", "attn_partials", "merge"]
+    stage_ms = {n: round(v * scale_rows * 1e3, 3) for n, v in zip(names, med)}
+    step_s = sum(med) * scale_rows
+    out = dict(kind="oracle", cores=orc.num_threads(), cpu_model=cpu_model(),
+               build="gcc -O3 -march=native -fopenmp, strict IEEE, fp64 accumulation",
+               rows_timed=len(rows), runs=len(runs), stage_ms=stage_ms,
+               step_ms=round(step_s * 1e3, 3),
+               sample=(f"{len(rows)} of {case.rows} rows (every {case.rows // len(rows)}th), "
+                       f"stage times scaled by {scale_rows:g}" if scale_rows > 1 else
+                       f"all {case.rows} rows, median of {len(runs)} pass(es)"))
+    scan_s = (med[0] + med[1]) * scale_rows
+    out["index_scan_GBps"] = round((alg["kidx"] + alg["qidx"]) / scan_s / 1e9, 3)
+    if case.prefill:
+        out["attn_tflops_with_merge"] = round(
+            alg["attn_flops"] / ((med[3] + med[4]) * scale_rows) / 1e12, 5)
+    else:
+        out["decode_tok_s"] = round(case.rows / step_s, 3)
+    return out
 
 
 def measured_peaks():
@@ -426,16 +500,20 @@ def summarize(cfg, case, r, peaks=None):
             res["attn_frac_of_measured_mfma"] = round(
                 res["attn_tflops_kernel_call"] / peaks["mfma_bf16_TFLOPs"], 4)
         res["attn_flops"] = a["attn_flops"]
-        # index scoring: the definition's FLOPs (every index vector separately) and
-        # the matrix-core FLOPs actually issued (qbar as bf16 hi + lo: 2 passes)
-        res["index_alg_tflops"] = round(a["index_flops"] / (t["index_score"] * 1e-3) / 1e12, 2)
-        mfma_flops = a["index_flops"] * 2 / case.n_idx
-        res["index_mfma_tflops"] = round(mfma_flops / (t["index_score"] * 1e-3) / 1e12, 2)
+        # index scoring contracts qbar = sum_j q_j (one vector per (row, group))
+        # with the visible key-index tokens: 2 d_idx FLOP per token, reported as
+        # index_qbar_tflops; the matrix cores take qbar as bf16 hi + lo, two
+        # passes, so they issue twice that (index_mfma_tflops, against the peak)
+        qbar_flops = a["index_flops"] / case.n_idx
+        res["index_qbar_tflops"] = round(qbar_flops / (t["index_score"] * 1e-3) / 1e12, 2)
+        res["index_mfma_tflops"] = round(2 * qbar_flops / (t["index_score"] * 1e-3) / 1e12, 2)
         res["index_mfma_frac"] = round(res["index_mfma_tflops"] / BF16_PEAK_TFLOPS, 4)
     else:
         res["decode_tok_s"] = round(case.rows / (r["ms_per_step"] * 1e-3), 1)
         step_bytes = a["kidx"] + a["qidx"] + a["kv_bytes"] + a["qo_bytes"]
         res["step_alg_GBps"] = round(step_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1)
+        res["step_hbm_frac"] = round(res["step_alg_GBps"] / HBM_PEAK_GBPS, 4)
+        res["step_alg_bytes"] = step_bytes
         attn_bytes = a["kv_bytes"] + a["qo_bytes"] // 2 + a["part_bytes"]
         res["decode_attn_GBps"] = round(attn_bytes / (t["attn"] * 1e-3) / 1e9, 1)
         res["decode_attn_hbm_frac"] = round(res["decode_attn_GBps"] / HBM_PEAK_GBPS, 4)
@@ -469,6 +547,17 @@ def main():
         print(f"[bench] workload {cfg}: {steps} steps", file=sys.stderr, flush=True)
         case, r = run_workload(cfg, steps, args.warmup, graph_replay=not args.eager_only)
         results[cfg] = summarize(cfg, case, r, peaks)
+        if not args.no_cpu_baseline:
+            # the oracle on the host cores, same inputs, after the GPU timing
+            print(f"[bench] workload {cfg}: cpu oracle", file=sys.stderr, flush=True)
+            cpu = cpu_oracle(cfg, case, r["alg"])
+            res = results[cfg]
+            if case.prefill:
+                cpu["gpu_over_cpu"] = round(res["attn_tflops_with_merge"] /
+                                            cpu["attn_tflops_with_merge"], 1)
+            else:
+                cpu["gpu_over_cpu"] = round(res["decode_tok_s"] / cpu["decode_tok_s"], 1)
+            res["cpu_oracle"] = cpu
         if cfg == main_cfg:
             main_case, main_run = case, r
         else:
@@ -513,9 +602,12 @@ def main():
         roofline["back_to_back_achieved"] = round(a["score_bytes"] / (btb * 1e-3) / 1e9, 1)
         roofline["back_to_back_frac"] = round(roofline["back_to_back_achieved"] / HBM_PEAK_GBPS, 4)
     cpu = None
-    if not args.no_cpu_baseline and main_case is not None and not main_case.prefill:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(main_case)
+    mc = m.get("cpu_oracle")
+    if mc:
+        cpu = dict(value=mc.get("decode_tok_s", mc.get("attn_tflops_with_merge")),
+                   unit="tok/s" if "decode_tok_s" in mc else "TFLOP/s", cores=mc["cores"],
+                   kind="oracle", cpu_model=mc["cpu_model"], sample=mc["sample"],
+                   stage_ms=mc["stage_ms"], build=mc["build"])
     value = main_case.rows * args.steps / (main_run["total_ms"] * 1e-3)
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tok/s", n_gpus=1, steps=args.steps,

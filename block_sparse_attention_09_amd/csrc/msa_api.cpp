@@ -73,6 +73,17 @@ msa_status_t check_view(const msa_view_t &v, const char *name) {
 
 hipStream_t as_stream(msa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
+// k and the selection size: k + 1 slots per (row, group) must stay far from
+// int32 overflow (the kernels index slots and pad loops with int), and the
+// whole selection rows * G * (k + 1) must fit an int32 element count.
+msa_status_t check_k(int32_t k, int32_t rows, int32_t G) {
+    REQUIRE(k >= 0 && k < (1 << 30), MSA_ERR_INVALID, "k = %d must be in [0, 2^30)", k);
+    REQUIRE((int64_t)rows * G * ((int64_t)k + 1) < (int64_t)INT32_MAX, MSA_ERR_INVALID,
+            "rows * G * (k + 1) = %lld must fit in int32",
+            (long long)((int64_t)rows * G * ((int64_t)k + 1)));
+    return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,7 +136,7 @@ msa_status_t msa_topk_blocks(const msa_dims_t *dims, int32_t rows, const float *
     msa_status_t st = check_dims(dims, false, false);
     if (st != MSA_OK) return st;
     REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
-    REQUIRE(k >= 0, MSA_ERR_INVALID, "k = %d must be >= 0", k);
+    if ((st = check_k(k, rows, dims->G)) != MSA_OK) return st;
     REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
     if (rows == 0) return ok();
     REQUIRE(scores && row_pos && sel, MSA_ERR_NULL, "scores, row_pos and sel are required");
@@ -142,7 +153,7 @@ msa_status_t msa_topk_blocks_paged(const msa_dims_t *dims, int32_t rows, const f
     msa_status_t st = check_dims(dims, false, false);
     if (st != MSA_OK) return st;
     REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
-    REQUIRE(k >= 0, MSA_ERR_INVALID, "k = %d must be >= 0", k);
+    if ((st = check_k(k, rows, dims->G)) != MSA_OK) return st;
     REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
     REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
     if (rows == 0) return ok();
@@ -241,11 +252,14 @@ msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
                                            msa_view_t vc, const int32_t *row_pos, float sm_scale,
                                            int32_t *sel, int32_t *page_table, void *o_part,
                                            float *lse_part, msa_stream_t stream) {
-    REQUIRE(k >= 0 && k < (1 << 30), MSA_ERR_INVALID, "k = %d must be >= 0", k);
+    REQUIRE(dims, MSA_ERR_NULL, "dims is NULL");
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    msa_status_t st = check_k(k, rows, dims->G);
+    if (st != MSA_OK) return st;
     REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
     REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
     const int32_t nslot = k + 1;
-    msa_status_t st = check_attn(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
+    st = check_attn(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
                                  sm_scale, o_part, lse_part);
     if (st != MSA_OK) return st;
     if (rows == 0) return ok();

@@ -135,7 +135,9 @@ msa_status_t msa_index_score(const msa_dims_t *dims, int32_t rows, const void *q
  *
  *   scores   fp32 [rows][G][score_stride] (as written by msa_index_score)
  *   row_pos  int32 [rows]
- *   k        0 <= k; nslot = k + 1 entries per (row, group)
+ *   k        0 <= k < 2^30; nslot = k + 1 entries per (row, group); the whole
+ *            selection rows * G * (k + 1) must be below 2^31 - 1
+ *            (MSA_ERR_INVALID otherwise, before anything is launched)
  *   sel      int32 [rows][G][k + 1] */
 msa_status_t msa_topk_blocks(const msa_dims_t *dims, int32_t rows, const float *scores,
                              int32_t score_stride, const int32_t *row_pos, int32_t k,

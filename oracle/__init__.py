@@ -31,18 +31,60 @@ _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 
 
+_FLAGS = ["-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+          # strict IEEE: no fast-math, no contraction into FMAs, so every
+          # build (portable or host-tuned) computes bit-identical results
+          "-ffp-contract=off", "-fno-fast-math"]
+
+
+def _compile(out: str, extra=()) -> str:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", *_FLAGS, *extra, _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
+    """Compile the portable oracle with gcc (-O3, OpenMP, strict IEEE)."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
-               _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
+        _compile(_LIB)
     return _LIB
 
 
+def build_native(out_dir: str) -> str:
+    """Compile a copy tuned for the host it runs on (-march=native) into
+    out_dir, for timing the oracle as a CPU baseline on that host; it computes
+    exactly what the portable build does.  Built where it runs, because a
+    -march=native binary may not execute on another CPU."""
+    os.makedirs(out_dir, exist_ok=True)
+    return _compile(os.path.join(out_dir, "libmsa_oracle_native.so"), ["-march=native"])
+
+
 _lib_handle = None
+
+
+def use_library(path: str) -> None:
+    """Route every oracle call through the library at path (e.g. build_native's)."""
+    global _lib_handle
+    _lib_handle = _bind(ctypes.CDLL(path))
+
+
+def _bind(lib):
+    lib.orc_index_score.argtypes = [_i32, _i32, _i32, _i32, _u16p, _u16p, _i64, _i64, _i64,
+                                    _i32p, _i32, _i32p, _i32p, _i32p, _i32, _f64p]
+    lib.orc_topk.argtypes = [_i32, _i32, _f32p, _i32, _i32p, _i32, _i32p]
+    lib.orc_page_table.argtypes = [_i32, _i32, _i32, _i32p, _i32p, _i32p, _i32, _i32p]
+    attn_args = [_i32, _i32, _i32, _i32, _u16p, _u16p, _i64, _i64, _i64,
+                 _u16p, _i64, _i64, _i64, _i32p, _i32p, _i32, _i32p, ctypes.c_double,
+                 _f64p, _f64p]
+    lib.orc_attn.argtypes = attn_args
+    lib.orc_attn_partials.argtypes = attn_args
+    lib.orc_lse_merge.argtypes = [_i32, _i32, _i32, _i32, _f64p, _f64p, _f64p, _f64p]
+    for f in (lib.orc_index_score, lib.orc_topk, lib.orc_page_table, lib.orc_attn,
+              lib.orc_attn_partials, lib.orc_lse_merge):
+        f.restype = None
+    return lib
 
 
 def _lib():
@@ -50,21 +92,7 @@ def _lib():
     if _lib_handle is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        lib.orc_index_score.argtypes = [_i32, _i32, _i32, _i32, _u16p, _u16p, _i64, _i64, _i64,
-                                        _i32p, _i32, _i32p, _i32p, _i32p, _i32, _f64p]
-        lib.orc_topk.argtypes = [_i32, _i32, _f32p, _i32, _i32p, _i32, _i32p]
-        lib.orc_page_table.argtypes = [_i32, _i32, _i32, _i32p, _i32p, _i32p, _i32, _i32p]
-        attn_args = [_i32, _i32, _i32, _i32, _u16p, _u16p, _i64, _i64, _i64,
-                     _u16p, _i64, _i64, _i64, _i32p, _i32p, _i32, _i32p, ctypes.c_double,
-                     _f64p, _f64p]
-        lib.orc_attn.argtypes = attn_args
-        lib.orc_attn_partials.argtypes = attn_args
-        lib.orc_lse_merge.argtypes = [_i32, _i32, _i32, _i32, _f64p, _f64p, _f64p, _f64p]
-        for f in (lib.orc_index_score, lib.orc_topk, lib.orc_page_table, lib.orc_attn,
-                  lib.orc_attn_partials, lib.orc_lse_merge):
-            f.restype = None
-        _lib_handle = lib
+        _lib_handle = _bind(ctypes.CDLL(_LIB))
     return _lib_handle
 
 

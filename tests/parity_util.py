@@ -3,8 +3,10 @@ the oracle on host copies of the same inputs, and compare with the stated
 tolerances.
 
 Tolerances (fixed by the method's accuracy targets):
-  scores     |S_gpu - S_ref| <= 1e-3 |S_ref| for finite S_ref (guard 1e-3 max|S_ref|
-             per row near 0); -inf exactly where the oracle has -inf
+  scores     |S_gpu - S_ref| <= max(1e-3 |S_ref|, floor) for finite S_ref, where the
+             absolute floor (score_floor) is the rounding bound of the kernels' own
+             fp32 arithmetic and only matters for scores near 0; -inf exactly where
+             the oracle has -inf
   selection  bit-exact, except near-tie rows (k-th and (k+1)-th oracle scores
              closer than 1e-3 relative), which must still pick a valid top set
   attention  max |o_gpu - o_ref| <= 1e-2 on the same selection; partial LSEs within
@@ -19,6 +21,7 @@ import torch
 
 import msa_synth
 import oracle
+from oracle import inputs as oracle_inputs
 
 BLK = 128
 SCORE_RTOL = 1e-3
@@ -75,44 +78,9 @@ def gpu_path(case, prefill=None, sel=None, pt=None, sm_scale=None):
                                         lse_part=lse_part, o=o, lse=lse).items()}
 
 
-def host_rows(case, rows):
-    """Host (oracle) inputs for a subset of rows: index and query tensors of those
-    rows, the key-index pages of their requests in a compact pool, and a block
-    table remapped onto it."""
-    rows = list(rows)
-    rr = case.row_req.cpu().numpy()[rows]
-    reqs = sorted(set(rr.tolist()))
-    bt_full = case.block_table.cpu().numpy()
-    ctx = case.ctx_len.cpu().numpy()
-    pages, bt = [], np.zeros((len(reqs), bt_full.shape[1]), np.int32)
-    for i, r in enumerate(reqs):
-        nblk = (int(ctx[r]) + BLK - 1) // BLK
-        bt[i, :nblk] = len(pages) + np.arange(nblk)
-        pages.extend(bt_full[r, :nblk].tolist())
-    pidx = torch.tensor(pages, dtype=torch.long, device=case.k_idx.device)
-    remap = {r: i for i, r in enumerate(reqs)}
-    lo = None
-    if case.blk_lo is not None:
-        lo = case.blk_lo.cpu().numpy()[reqs]
-    ridx = torch.tensor(rows, dtype=torch.long, device=case.q.device)
-    return dict(
-        q_idx=msa_synth.bits(case.q_idx.index_select(0, ridx)),
-        q=msa_synth.bits(case.q.index_select(0, ridx)),
-        k_idx=msa_synth.bits(case.k_idx.index_select(0, pidx)),
-        bt=bt, row_req=np.array([remap[int(r)] for r in rr], np.int32),
-        row_pos=case.row_pos.cpu().numpy()[rows], blk_lo=lo)
-
-
-def host_kv_pages(case, pt_rows: np.ndarray):
-    """Compact host K/V pools holding only the pages a page table references,
-    plus that page table remapped onto them."""
-    used = sorted(set(int(p) for p in pt_rows.ravel() if p >= 0))
-    remap = np.full(max(used) + 1 if used else 1, -1, np.int64)
-    remap[used] = np.arange(len(used))
-    pt_c = np.where(pt_rows >= 0, remap[np.maximum(pt_rows, 0)], -1).astype(np.int32)
-    pidx = torch.tensor(used, dtype=torch.long, device=case.k_cache.device)
-    return (msa_synth.bits(case.k_cache.index_select(0, pidx)),
-            msa_synth.bits(case.v_cache.index_select(0, pidx)), pt_c)
+# host copies of the rows and pages the oracle needs (marshalling only)
+host_rows = oracle_inputs.host_rows
+host_kv_pages = oracle_inputs.host_kv_pages
 
 
 def oracle_scores(case, rows):
@@ -134,18 +102,73 @@ def oracle_attn(case, rows, sel_rows, pt_rows, sm_scale=None):
 
 
 # ----------------------------------------------------------------------------- comparisons
-def check_scores(s_gpu: np.ndarray, s_ref: np.ndarray):
+U32 = 2.0 ** -24      # unit roundoff of fp32
+U_BF16 = 2.0 ** -9    # unit roundoff of bf16 (round to nearest even)
+
+
+def score_floor(case, rows):
+    """Absolute error floor of every block score of the given rows, [rows][G][1].
+
+    Both scorers compute S = max_t (qbar . k_t) / sqrt(d_idx) with
+    qbar = sum_j q_j formed in fp32 from the bf16 index vectors and the dot
+    product accumulated in fp32 (the prefill scorer feeds qbar to the matrix
+    cores as bf16 hi + lo, a residual of at most U_BF16^2 |qbar_d| per dim).
+    Standard rounding-error bounds for these steps, with
+    A = sum_d |qbar_d| |k_d| <= |qbar|_2 |k|_2 and
+    B = sum_j sum_d |q_jd| |k_d| <= (sum_j |q_j|_2) |k|_2 (Cauchy-Schwarz):
+        dot product of d_idx terms        d_idx U32 A
+        sum of the n_idx index vectors    n_idx U32 B
+        hi + lo residual                  U_BF16^2 A
+        final scale and max               2 U32 A
+    kmax2 = the largest |k_t|_2 over the finite key-index rows of the cache
+    bounds |k|_2 for every token.  The floor is that sum / sqrt(d_idx): on
+    N(0, 1) data about 4e-4, against block scores of about 5, so the strict
+    1e-3 relative bound decides everywhere except at scores near 0 (e.g. an
+    own block with one visible token)."""
+    rows = list(rows)
+    ridx = torch.tensor(rows, dtype=torch.long, device=case.q_idx.device)
+    q = oracle.bf16_bits_to_f64(msa_synth.bits(case.q_idx.index_select(0, ridx)))
+    qbar2 = np.linalg.norm(q.sum(axis=2), axis=-1)                 # [rows][G]
+    qsum2 = np.linalg.norm(q, axis=-1).sum(axis=2)                 # [rows][G]
+    kmax2 = _visible_key_index_norm(case)
+    eps_a = (case.d_idx + 2) * U32 + U_BF16 ** 2
+    floor = (eps_a * qbar2 + case.n_idx * U32 * qsum2) * kmax2 / math.sqrt(case.d_idx)
+    return floor[..., None]
+
+
+def _visible_key_index_norm(case, chunk=2048):
+    """max over the written cache slots of |k_idx[page][g][t]|_2 (slots past a
+    request's last token may hold poison and are never scored)."""
+    P = case.k_idx.shape[0]
+    kn = torch.empty(case.k_idx.shape[:3], dtype=torch.float32, device=case.k_idx.device)
+    for p0 in range(0, P, chunk):
+        kn[p0:p0 + chunk] = torch.linalg.vector_norm(case.k_idx[p0:p0 + chunk].float(), dim=-1)
+    bt = case.block_table.cpu().numpy()
+    for r, L in enumerate(case.ctx_len.cpu().numpy().tolist()):
+        if L % BLK:
+            kn[int(bt[r, (L - 1) // BLK]), :, L % BLK:] = 0
+    return float(torch.nan_to_num(kn, nan=0.0, posinf=0.0).max())
+
+
+def check_scores(s_gpu: np.ndarray, s_ref: np.ndarray, floor):
+    """Scores within max(1e-3 |S_ref|, floor), -inf exactly where the oracle has
+    it; returns the worst relative error among scores the relative bound
+    governs (|S_ref| >= floor / 1e-3)."""
     s_gpu = np.asarray(s_gpu, np.float64)
     ninf_ref = np.isneginf(s_ref)
     assert np.array_equal(np.isneginf(s_gpu), ninf_ref), "-inf pattern differs"
     fin = ~ninf_ref
-    guard = SCORE_RTOL * np.max(np.where(fin, np.abs(s_ref), 0), axis=-1, keepdims=True)
-    tol = np.maximum(SCORE_RTOL * np.abs(s_ref), guard)
+    floor = np.broadcast_to(np.asarray(floor, np.float64), s_ref.shape)
+    tol = np.maximum(SCORE_RTOL * np.abs(s_ref), floor)
     err = np.where(fin, np.abs(s_gpu - np.where(fin, s_ref, 0)), 0)
     bad = err > tol
-    assert not bad.any(), f"{bad.sum()} scores out of tolerance, worst rel " \
-                          f"{np.max(err / np.maximum(np.abs(s_ref), 1e-30)):.3g}"
-    return float(np.max(np.where(fin, err / np.maximum(np.abs(s_ref), 1e-30), 0)))
+    rel = np.where(fin & (np.abs(s_ref) * SCORE_RTOL >= floor),
+                   err / np.maximum(np.abs(s_ref), 1e-30), 0)
+    worst = float(rel.max()) if rel.size else 0.0
+    assert not bad.any(), f"{bad.sum()} scores out of tolerance, worst rel {worst:.3g}, " \
+                          f"worst abs near 0 {float(np.max(np.where(bad, err, 0))):.3g}"
+    print(f"  scores: {int(fin.sum())} finite, worst relative error {worst:.3g}", flush=True)
+    return worst
 
 
 def check_selection(sel_gpu, sel_ref, s_ref, row_pos, k):

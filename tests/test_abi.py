@@ -114,6 +114,22 @@ def test_topk_and_page_table_validation(lib):
                  None) == MSA_OK
 
 
+@pytest.mark.parametrize("k,rows", [(2 ** 31 - 1, 1), (2 ** 30, 1), (2 ** 28, 8)])
+def test_topk_rejects_huge_k(lib, k, rows):
+    """k near INT32_MAX (k + 1 would overflow the kernels' slot loops) and
+    selections beyond an int32 element count are refused before any launch,
+    by every call that selects."""
+    d = _dims()
+    assert lib.msa_topk_blocks(ctypes.byref(d), rows, FAKE, 4, FAKE, k, FAKE,
+                               None) == MSA_ERR_INVALID
+    assert b"k" in lib.msa_last_error()
+    assert lib.msa_topk_blocks_paged(ctypes.byref(d), rows, FAKE, 4, FAKE, k, None, FAKE, 4,
+                                     FAKE, FAKE, None) == MSA_ERR_INVALID
+    assert lib.msa_sparse_attn_decode_select(
+        ctypes.byref(d), rows, FAKE, 4, k, None, FAKE, 4, FAKE, _view(), _view(), FAKE,
+        ctypes.c_float(0.088), FAKE, FAKE, FAKE, FAKE, None) == MSA_ERR_INVALID
+
+
 def _decode(lib, dims, **kw):
     a = dict(rows=1, q=FAKE, k=_view(), v=_view(), sel=FAKE, pt=FAKE, nslot=3, rp=FAKE,
              scale=0.088, o=FAKE, lse=FAKE)

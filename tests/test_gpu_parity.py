@@ -42,7 +42,8 @@ SMALL = {
     "lo-above-own": dict(seed=109, ctx_lens=[900, 1400, 2000], G=2, Hg=4, d_idx=64, k=3,
                          lo_frac=1.5),
     # long score rows in a small batch: 782 blocks per row (the one-kernel selection +
-    # decode attention with 16 scores per lane), 1,954 (past its limit: two kernels)
+    # decode attention, its 256 threads holding 4 scores each), 1,954 (past its
+    # 1,024-block limit: two kernels)
     "long-782": dict(seed=111, ctx_lens=[100_000, 65_000], G=2, Hg=4, d_idx=64, k=8),
     "long-1954": dict(seed=112, ctx_lens=[250_000, 131_073], G=2, Hg=4, d_idx=64, k=16),
     # either side of the select call's one-round rule (8 groups x 17 slots: 9 rows =
@@ -61,7 +62,7 @@ SMALL = {
 def _full_compare(case, res, rows=None):
     rows = list(range(case.rows)) if rows is None else list(rows)
     s_ref = pu.oracle_scores(case, rows)
-    rel = pu.check_scores(res["scores"].numpy()[rows], s_ref)
+    rel = pu.check_scores(res["scores"].numpy()[rows], s_ref, pu.score_floor(case, rows))
     sel_ref = oracle.topk(s_ref.astype(np.float32), case.row_pos.cpu().numpy()[rows], case.k)
     ntie = pu.check_selection(res["sel"].numpy()[rows], sel_ref, s_ref,
                               case.row_pos.cpu().numpy()[rows], case.k)
@@ -289,6 +290,12 @@ def test_kv_cache_in_pinned_host_memory():
         b = pu.gpu_path(host)
         for key in a:
             assert torch.equal(a[key], b[key]), key
+        # and the host-memory result itself against the oracle
+        rows = list(range(case.rows))
+        _full_compare(host, b)
+        op, lp, o, lse = pu.oracle_attn(host, rows, b["sel"].numpy(), b["pt"].numpy())
+        pu.check_partials(b["o_part"], b["lse_part"], op, lp)
+        pu.check_output(b["o"], b["lse"], o, lse)
 
 
 def test_gather_pages_then_decode():
@@ -307,6 +314,8 @@ def test_gather_pages_then_decode():
                                         row_req=case.row_req)
     ref = msa.msa_sparse_attn_decode(d, case.q, case.k_cache, case.v_cache, sel, pt,
                                      case.row_pos, scale)
+    rows = list(range(case.rows))
+    op, lp, o_ref, lse_ref = pu.oracle_attn(case, rows, sel.cpu().numpy(), pt.cpu().numpy())
     for where in ("device", "host"):
         kc, vc = case.k_cache, case.v_cache
         if where == "host":
@@ -319,6 +328,10 @@ def test_gather_pages_then_decode():
         units = torch.arange(ptc.numel(), dtype=torch.int32).view_as(ptc)
         assert torch.equal(pptc[ptc >= 0], units[ptc >= 0]), where
         assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1]), where
+        # the pool's partials and their merge against the oracle on the cache
+        pu.check_partials(out[0].cpu(), out[1].cpu(), op, lp)
+        o, lse = msa.msa_lse_merge(out[0], out[1])
+        pu.check_output(o.cpu(), lse.cpu(), o_ref, lse_ref)
 
 
 def test_host_cache_must_be_pinned():
