@@ -9,7 +9,7 @@ the first call raises.
 Calls (same names and meaning as the C functions):
     msa_index_score, msa_topk_blocks, msa_build_page_table, msa_topk_blocks_paged,
     msa_sparse_attn_decode, msa_sparse_attn_decode_select, msa_prefill_workspace_size,
-    msa_sparse_attn_prefill,
+    msa_sparse_attn_prefill, msa_sparse_attn_prefill_noalloc,
     msa_lse_merge, msa_version, msa_gather_pages
 Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout)
 Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
@@ -32,6 +32,7 @@ from .binding import (  # noqa: F401
     msa_sparse_attn_decode,
     msa_sparse_attn_decode_select,
     msa_sparse_attn_prefill,
+    msa_sparse_attn_prefill_noalloc,
     msa_topk_blocks,
     msa_topk_blocks_paged,
     msa_version,

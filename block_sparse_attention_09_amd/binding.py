@@ -54,6 +54,8 @@ _SIGS = {
     "msa_prefill_workspace_size": [_DIMS, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
     "msa_sparse_attn_prefill": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
                                 ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
+    "msa_sparse_attn_prefill_noalloc": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
+                                        ctypes.c_float, _P, _P, _P],
     "msa_lse_merge": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     "msa_gather_pages": [_DIMS, _I32, _P, _I32, View, View, _P, _P, _P, _P],
     "msa_peak_stream_read": [_P, ctypes.c_size_t, _P, _P],
@@ -298,6 +300,26 @@ def msa_sparse_attn_prefill(dims: Dims, q, k_cache, v_cache, sel, page_table, ro
                                           scale, _ptr(workspace), workspace.numel(),
                                           _ptr(o_part), _ptr(lse_part), _stream(stream)),
            "msa_sparse_attn_prefill")
+    return o_part, lse_part
+
+
+def msa_sparse_attn_prefill_noalloc(dims: Dims, q, k_cache, v_cache, sel, page_table, row_pos,
+                                    num_pages, sm_scale=None, o_part=None, lse_part=None,
+                                    stream=None):
+    """msa_sparse_attn_prefill without a workspace: the library's static device
+    scratch serves instead (for callers that cannot allocate; pass o_part and
+    lse_part to allocate nothing on this side either)."""
+    _need(q, torch.bfloat16, "q", True)
+    _i32(sel, "sel"), _i32(page_table, "page_table"), _i32(row_pos, "row_pos")
+    rows, nslot = q.shape[0], sel.shape[2]
+    o_part, lse_part = _attn_out(q, nslot, o_part, lse_part)
+    scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dims.D))
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_sparse_attn_prefill_noalloc(ctypes.byref(dims), rows, _ptr(q), kv[0],
+                                                  kv[1], _ptr(sel), _ptr(page_table), nslot,
+                                                  _ptr(row_pos), num_pages, scale, _ptr(o_part),
+                                                  _ptr(lse_part), _stream(stream)),
+           "msa_sparse_attn_prefill_noalloc")
     return o_part, lse_part
 
 

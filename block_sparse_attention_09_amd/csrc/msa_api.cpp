@@ -318,6 +318,33 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t rows, const
                       "msa_sparse_attn_prefill");
 }
 
+msa_status_t msa_sparse_attn_prefill_noalloc(const msa_dims_t *dims, int32_t rows,
+                                             const void *q, msa_view_t k, msa_view_t v,
+                                             const int32_t *sel, const int32_t *page_table,
+                                             int32_t nslot, const int32_t *row_pos,
+                                             int32_t num_pages, float sm_scale, void *o_part,
+                                             float *lse_part, msa_stream_t stream) {
+    msa_status_t st = check_attn(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale,
+                                 o_part, lse_part);
+    if (st != MSA_OK) return st;
+    REQUIRE(num_pages >= 1, MSA_ERR_INVALID, "num_pages = %d must be >= 1", num_pages);
+    REQUIRE((int64_t)dims->G * num_pages < ((int64_t)1 << 31) - 1, MSA_ERR_INVALID,
+            "G * num_pages must fit in int32");
+    if (rows == 0) return ok();
+    const size_t need = msa::prefill_workspace_bytes(rows, dims->G, nslot, num_pages);
+    REQUIRE(need <= msa::kNoallocScratchBytes, MSA_ERR_WORKSPACE,
+            "this prefill needs %zu bytes of workspace, beyond the %zu-byte static scratch of "
+            "the allocation-free call (use msa_sparse_attn_prefill with a workspace)",
+            need, msa::kNoallocScratchBytes);
+    void *ws = nullptr;
+    const hipError_t e = msa::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "msa_sparse_attn_prefill_noalloc: scratch address");
+    const msa::AttnArgs a =
+        attn_args(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale, o_part, lse_part);
+    return hip_status(msa::launch_attn_prefill(a, num_pages, ws, as_stream(stream)),
+                      "msa_sparse_attn_prefill_noalloc");
+}
+
 msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D, const void *o_part,
                            const float *lse_part, void *o, float *lse, msa_stream_t stream) {
     REQUIRE(rows >= 0 && H >= 1 && nslot >= 1, MSA_ERR_INVALID,

@@ -139,6 +139,12 @@ hipError_t launch_attn_decode_select(const AttnArgs &a, const SelectArgs &sa, hi
 int decode_select_capacity(int Hg);
 
 size_t prefill_workspace_bytes(int rows, int G, int nslot, int num_pages);
+
+// Scratch of the allocation-free prefill entry point: a static device array of
+// this many bytes (MSA_NOALLOC_SCRATCH_BYTES in msa.h); noalloc_scratch gives
+// its address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = MSA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_attn_prefill(const AttnArgs &a, int num_pages, void *workspace,
                                hipStream_t stream);
 

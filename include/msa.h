@@ -270,6 +270,31 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t rows, const
                                      void *workspace, size_t workspace_bytes, void *o_part,
                                      float *lse_part, msa_stream_t stream);
 
+/* ------------------------------------------------------------------ a8 / a9, no allocation
+ * msa_sparse_attn_prefill_noalloc -- msa_sparse_attn_prefill for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid allocation): it takes no workspace and allocates nothing.
+ *
+ * Same arguments, results and errors as msa_sparse_attn_prefill without
+ * workspace / workspace_bytes; the results are bit-identical to it.  The
+ * workspace lives instead in a static device array of
+ * MSA_NOALLOC_SCRATCH_BYTES bytes that each GPU the library runs on holds
+ * until the process ends.  A call whose workspace
+ * (msa_prefill_workspace_size) exceeds it fails with MSA_ERR_WORKSPACE before
+ * anything is launched: 16 MiB covers e.g. 8,192 query rows x 8 groups x 17
+ * slots on 544 pages (about 9 MB).  Nothing in the array needs to start
+ * cleared; every call rewrites what it reads.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (concurrent streams, or
+ * threads) race on it and must be serialised by the caller. */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+msa_status_t msa_sparse_attn_prefill_noalloc(const msa_dims_t *dims, int32_t rows,
+                                             const void *q, msa_view_t k, msa_view_t v,
+                                             const int32_t *sel, const int32_t *page_table,
+                                             int32_t nslot, const int32_t *row_pos,
+                                             int32_t num_pages, float sm_scale, void *o_part,
+                                             float *lse_part, msa_stream_t stream);
+
 /* ------------------------------------------------------------------ a5 / a10
  * msa_lse_merge -- log-sum-exp reduction of per-block partials.
  * Pages: the final reduction rescales the partial O outputs by their
