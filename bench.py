@@ -455,12 +455,18 @@ def measured_peaks():
     iters = 16384
     flops = msa.msa_peak_mfma_bf16(iters, sink)
     t_mfma = best(lambda: msa.msa_peak_mfma_bf16(iters, sink), 3)
+    iters_r = 4096
+    flops_r = msa.msa_peak_mfma_bf16_random(iters_r, sink)
+    t_mfma_r = best(lambda: msa.msa_peak_mfma_bf16_random(iters_r, sink), 3)
     return dict(stream_read_GBps=round(nbytes / (t_read * 1e-3) / 1e9, 1),
                 mfma_bf16_TFLOPs=round(flops / (t_mfma * 1e-3) / 1e12, 1),
+                mfma_bf16_random_TFLOPs=round(flops_r / (t_mfma_r * 1e-3) / 1e12, 1),
                 method=("msa_peak_stream_read over 4 GiB (a workgroup per 64 KB chunk, 8 "
                         "non-temporal 16-B loads in flight per thread); msa_peak_mfma_bf16: 4 "
-                        "independent 32x32x16 bf16 MFMA chains per wave, 2 waves per SIMD; best "
-                        "of 5 and 3 launches"))
+                        "independent 32x32x16 bf16 MFMA chains per wave on fixed operands, 2 "
+                        "waves per SIMD; msa_peak_mfma_bf16_random: the same on pseudo-random "
+                        "unit-variance operands (the matrix cores' rate depends on the data); "
+                        "best of 5, 3 and 3 launches"))
 
 
 def summarize(cfg, case, r, peaks=None):
@@ -499,6 +505,8 @@ def summarize(cfg, case, r, peaks=None):
         if peaks:
             res["attn_frac_of_measured_mfma"] = round(
                 res["attn_tflops_kernel_call"] / peaks["mfma_bf16_TFLOPs"], 4)
+            res["attn_frac_of_random_operand_mfma"] = round(
+                res["attn_tflops_kernel_call"] / peaks["mfma_bf16_random_TFLOPs"], 4)
         res["attn_flops"] = a["attn_flops"]
         # index scoring contracts qbar = sum_j q_j (one vector per (row, group))
         # with the visible key-index tokens: 2 d_idx FLOP per token, reported as
@@ -508,6 +516,9 @@ def summarize(cfg, case, r, peaks=None):
         res["index_qbar_tflops"] = round(qbar_flops / (t["index_score"] * 1e-3) / 1e12, 2)
         res["index_mfma_tflops"] = round(2 * qbar_flops / (t["index_score"] * 1e-3) / 1e12, 2)
         res["index_mfma_frac"] = round(res["index_mfma_tflops"] / BF16_PEAK_TFLOPS, 4)
+        if peaks:
+            res["index_mfma_frac_of_random_operand_mfma"] = round(
+                res["index_mfma_tflops"] / peaks["mfma_bf16_random_TFLOPs"], 4)
     else:
         res["decode_tok_s"] = round(case.rows / (r["ms_per_step"] * 1e-3), 1)
         step_bytes = a["kidx"] + a["qidx"] + a["kv_bytes"] + a["qo_bytes"]
@@ -564,7 +575,7 @@ def main():
             del case
             torch.cuda.empty_cache()
 
-    if not args.no_kv_on_host and not args.eager_only:
+    if not args.no_kv_on_host and not args.eager_only and not main_case.prefill:
         print(f"[bench] workload {main_cfg} with K/V in pinned host memory", file=sys.stderr,
               flush=True)
         case, r = run_workload(main_cfg, 20, args.warmup, kv_on_host=True)

@@ -13,7 +13,7 @@ Calls (same names and meaning as the C functions):
     msa_lse_merge, msa_version, msa_gather_pages
 Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout)
 Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
-    msa_peak_stream_read, msa_peak_mfma_bf16
+    msa_peak_stream_read, msa_peak_mfma_bf16, msa_peak_mfma_bf16_random
 """
 from .binding import (  # noqa: F401
     Dims,
@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     msa_index_score,
     msa_lse_merge,
     msa_peak_mfma_bf16,
+    msa_peak_mfma_bf16_random,
     msa_peak_stream_read,
     msa_prefill_workspace_size,
     msa_sparse_attn_decode,

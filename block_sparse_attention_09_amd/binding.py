@@ -60,6 +60,7 @@ _SIGS = {
     "msa_gather_pages": [_DIMS, _I32, _P, _I32, View, View, _P, _P, _P, _P],
     "msa_peak_stream_read": [_P, ctypes.c_size_t, _P, _P],
     "msa_peak_mfma_bf16": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
+    "msa_peak_mfma_bf16_random": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
 }
 
 _lib = None
@@ -378,4 +379,13 @@ def msa_peak_mfma_bf16(iters: int, sink: torch.Tensor, stream=None) -> float:
     flops = ctypes.c_double(0.0)
     _check(load().msa_peak_mfma_bf16(iters, _ptr(sink), ctypes.byref(flops), _stream(stream)),
            "msa_peak_mfma_bf16")
+    return flops.value
+
+
+def msa_peak_mfma_bf16_random(iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch the bf16 matrix-core loop probe on pseudo-random operands; returns its FLOPs."""
+    _need(sink, torch.float32, "sink")
+    flops = ctypes.c_double(0.0)
+    _check(load().msa_peak_mfma_bf16_random(iters, _ptr(sink), ctypes.byref(flops),
+                                            _stream(stream)), "msa_peak_mfma_bf16_random")
     return flops.value

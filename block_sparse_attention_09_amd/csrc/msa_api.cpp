@@ -399,4 +399,12 @@ msa_status_t msa_peak_mfma_bf16(int32_t iters, float *sink, double *flops, msa_s
                       "msa_peak_mfma_bf16");
 }
 
+msa_status_t msa_peak_mfma_bf16_random(int32_t iters, float *sink, double *flops,
+                                       msa_stream_t stream) {
+    REQUIRE(iters >= 1, MSA_ERR_INVALID, "iters = %d must be >= 1", iters);
+    REQUIRE(sink && flops, MSA_ERR_NULL, "sink and flops are required");
+    return hip_status(msa::launch_peak_mfma_bf16_random(iters, sink, flops, as_stream(stream)),
+                      "msa_peak_mfma_bf16_random");
+}
+
 }  // extern "C"

@@ -1,7 +1,11 @@
 // peaks.hip -- measured machine peaks (gfx950), the reference points the MSA
 // kernels' rooflines are read against besides the published ones: a plain
-// streaming read of a large buffer (HBM) and a register-resident bf16 MFMA
-// loop (matrix cores).  Neither is part of the MSA path.
+// streaming read of a large buffer (HBM) and register-resident bf16 MFMA loops
+// (matrix cores), one on fixed low-entropy operands and one on pseudo-random
+// operands of unit variance like the MSA workloads' values: the matrix cores'
+// sustained rate depends on the operand bits they toggle (the chip lowers its
+// rate under the higher power draw of random data).  None is part of the MSA
+// path.
 #include "msa_internal.h"
 
 namespace msa {
@@ -62,6 +66,49 @@ __global__ __launch_bounds__(kPeakThreads) void mfma_loop_kernel(int iters,
     if (s == 1.2345f) sink[0] = s;
 }
 
+// Pseudo-random operands: each lane holds 8 A and 8 B fragments of roughly
+// normal bf16 values (a sum of four uniforms from an integer hash of the lane,
+// fragment and element), and two accumulation chains cycle through them, so
+// consecutive MFMAs see different random operands as a real contraction does.
+__device__ __forceinline__ uint32_t peak_hash(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+__device__ __forceinline__ float peak_normalish(uint32_t key) {
+    const uint32_t h0 = peak_hash(key), h1 = peak_hash(key ^ 0x5bd1e995u);
+    const float u = (float)(h0 & 0xffff) + (float)(h0 >> 16) + (float)(h1 & 0xffff) +
+                    (float)(h1 >> 16);
+    // four uniforms on [0, 65536): mean 131070, variance 4 * 65536^2 / 12
+    return (u - 131070.f) * (1.7320508f / 65536.f);
+}
+
+__global__ __launch_bounds__(kPeakThreads) void mfma_random_loop_kernel(int iters,
+                                                                        float *__restrict__ sink) {
+    const uint32_t t = blockIdx.x * kPeakThreads + threadIdx.x;
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[i][e] = (__bf16)peak_normalish((t * 8u + i) * 16u + e);
+            b[i][e] = (__bf16)peak_normalish((t * 8u + i) * 16u + 8u + e + 0x40000000u);
+        }
+    f32x16 c0 = {}, c1 = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c0 = mfma32(a[i], b[i], c0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c1 = mfma32(a[i], b[(i + 3) & 7], c1);
+    }
+    const float s = c0[0] + c1[1];
+    if (s == 1.2345f) sink[0] = s;
+}
+
 }  // namespace
 
 hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
@@ -81,6 +128,19 @@ hipError_t launch_peak_mfma_bf16(int iters, float *sink, double *flops, hipStrea
     const int grid = 2 * cus;  // two workgroups per CU: two waves per SIMD
     *flops = (double)grid * (kPeakThreads / kWave) * (double)iters * 4.0 * (2.0 * 32 * 32 * 16);
     hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(kPeakThreads), 0, stream, iters, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_peak_mfma_bf16_random(int iters, float *sink, double *flops,
+                                       hipStream_t stream) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = 2 * cus;  // two workgroups per CU: two waves per SIMD
+    *flops = (double)grid * (kPeakThreads / kWave) * (double)iters * 16.0 * (2.0 * 32 * 32 * 16);
+    hipLaunchKernelGGL(mfma_random_loop_kernel, dim3(grid), dim3(kPeakThreads), 0, stream, iters,
+                       sink);
     return hipGetLastError();
 }
 

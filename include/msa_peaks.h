@@ -3,7 +3,7 @@
  *
  * The MSA kernels are read against the published MI355X peaks (8 TB/s HBM,
  * 2.5 PFLOP/s dense bf16) and against what this device actually sustains with
- * nothing else in the way.  These two probes measure the latter; they are
+ * nothing else in the way.  These probes measure the latter; they are
  * measurement aids, not steps of the MSA path, and follow the conventions of
  * msa.h (status codes, msa_last_error(), asynchronous on the caller's stream,
  * no allocation, device pointers unless stated).
@@ -34,6 +34,18 @@ msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
  * dense bf16 rate.  `sink` as above.
  * Errors: MSA_ERR_INVALID (iters < 1), MSA_ERR_NULL, MSA_ERR_HIP. */
 msa_status_t msa_peak_mfma_bf16(int32_t iters, float *sink, double *flops, msa_stream_t stream);
+
+/* The same loop on pseudo-random operands: each lane holds 8 A and 8 B
+ * fragments of roughly normal bf16 values (unit variance, from an integer hash
+ * of the lane and element), and each wave runs `iters` iterations of two
+ * accumulation chains of 8 MFMAs cycling through them.  The matrix cores'
+ * sustained rate depends on the operand data (the chip lowers its rate under
+ * the power draw of random bits), so this is the rate a contraction of
+ * N(0,1)-like values can reach, below the fixed-operand loop above.  *flops
+ * and `sink` as above.
+ * Errors: MSA_ERR_INVALID (iters < 1), MSA_ERR_NULL, MSA_ERR_HIP. */
+msa_status_t msa_peak_mfma_bf16_random(int32_t iters, float *sink, double *flops,
+                                       msa_stream_t stream);
 
 #ifdef __cplusplus
 }
