@@ -8,21 +8,29 @@ the first call raises.
 
 Calls (same names and meaning as the C functions):
     msa_index_score, msa_topk_blocks, msa_build_page_table, msa_topk_blocks_paged,
-    msa_sparse_attn_decode, msa_sparse_attn_decode_select, msa_prefill_workspace_size,
+    msa_sparse_attn_decode, msa_sparse_attn_decode_select, msa_decode_step,
+    msa_prefill_workspace_size,
     msa_sparse_attn_prefill, msa_sparse_attn_prefill_noalloc,
     msa_lse_merge, msa_version, msa_gather_pages
-Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout)
+Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout);
+MSA_STEP_AUTO, MSA_STEP_ONE_LAUNCH, MSA_STEP_SEPARATE (msa_decode_step modes),
+decode_step_sync_words (length of its int32 sync array)
 Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
     msa_peak_stream_read, msa_peak_mfma_bf16, msa_peak_mfma_bf16_random
 """
 from .binding import (  # noqa: F401
+    MSA_STEP_AUTO,
+    MSA_STEP_ONE_LAUNCH,
+    MSA_STEP_SEPARATE,
     Dims,
     MSAError,
+    decode_step_sync_words,
     View,
     empty_lse_part,
     lib_path,
     load,
     msa_build_page_table,
+    msa_decode_step,
     msa_gather_pages,
     msa_index_score,
     msa_lse_merge,

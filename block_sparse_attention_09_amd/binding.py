@@ -51,6 +51,8 @@ _SIGS = {
                                _P, _P, _P],
     "msa_sparse_attn_decode_select": [_DIMS, _I32, _P, _I32, _I32, _P, _P, _I32, _P, View, View,
                                       _P, ctypes.c_float, _P, _P, _P, _P, _P],
+    "msa_decode_step": [_DIMS, _I32, _P, View, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, View,
+                        View, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "msa_prefill_workspace_size": [_DIMS, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
     "msa_sparse_attn_prefill": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
                                 ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
@@ -274,6 +276,62 @@ def msa_sparse_attn_decode_select(dims: Dims, scores, k, block_table, q, k_cache
         _ptr(sel), _ptr(page_table), _ptr(o_part), _ptr(lse_part), _stream(stream)),
         "msa_sparse_attn_decode_select")
     return sel, page_table, o_part, lse_part
+
+
+MSA_STEP_AUTO, MSA_STEP_ONE_LAUNCH, MSA_STEP_SEPARATE = 0, 1, 2
+
+
+def decode_step_sync_words(rows, G) -> int:
+    """Length of msa_decode_step's int32 sync array (MSA_DECODE_STEP_SYNC_WORDS)."""
+    return 4 + 2 * rows * G
+
+
+def msa_decode_step(dims: Dims, q_idx, k_idx, block_table, row_pos, score_stride, k, q,
+                    k_cache, v_cache, row_req=None, blk_lo=None, num_reqs=None, sm_scale=None,
+                    mode=MSA_STEP_AUTO, sync=None, scores=None, sel=None, page_table=None,
+                    o_part=None, lse_part=None, o=None, lse=None, stream=None):
+    """The whole decode step (scores, selection, page table, slot partials and
+    their merge); returns (scores, sel, page_table, o_part, lse_part, o, lse).
+    sync: int32 device tensor of decode_step_sync_words(rows, G) zeros (left zero
+    by every call); when None and mode is not MSA_STEP_SEPARATE a zeroed one is
+    allocated for the call (pass a persistent one to avoid that)."""
+    _need(q_idx, torch.bfloat16, "q_idx", True)
+    _need(q, torch.bfloat16, "q", True)
+    _i32(block_table, "block_table"), _i32(row_pos, "row_pos")
+    _i32(row_req, "row_req"), _i32(blk_lo, "blk_lo")
+    rows, H, D = q.shape
+    dev = q.device
+    if scores is None:
+        scores = torch.empty((rows, dims.G, score_stride), dtype=torch.float32, device=dev)
+    if sel is None:
+        sel = torch.empty((rows, dims.G, k + 1), dtype=torch.int32, device=dev)
+    if page_table is None:
+        page_table = torch.empty_like(sel)
+    _need(scores, torch.float32, "scores", True)
+    _i32(sel, "sel"), _i32(page_table, "page_table")
+    o_part, lse_part = _attn_out(q, k + 1, o_part, lse_part)
+    if o is None:
+        o = torch.empty((rows, H, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    _need(o, torch.bfloat16, "o", True)
+    _need(lse, torch.float32, "lse", True)
+    if sync is None and mode != MSA_STEP_SEPARATE:
+        sync = torch.zeros(decode_step_sync_words(rows, dims.G), dtype=torch.int32, device=dev)
+    if sync is not None:
+        _i32(sync, "sync")
+        if sync.numel() < decode_step_sync_words(rows, dims.G):
+            raise ValueError("sync: too short (decode_step_sync_words)")
+    nreq = int(num_reqs if num_reqs is not None else block_table.shape[0])
+    scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dims.D))
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_decode_step(
+        ctypes.byref(dims), rows, _ptr(q_idx), view_of(k_idx), _ptr(block_table),
+        block_table.shape[1], _ptr(row_req), _ptr(row_pos), _ptr(blk_lo), nreq, score_stride, k,
+        _ptr(q), kv[0], kv[1], scale, _ptr(scores), _ptr(sel), _ptr(page_table), _ptr(o_part),
+        _ptr(lse_part), _ptr(o), _ptr(lse), _ptr(sync), int(mode), _stream(stream)),
+        "msa_decode_step")
+    return scores, sel, page_table, o_part, lse_part, o, lse
 
 
 def msa_prefill_workspace_size(dims: Dims, rows, nslot, num_pages) -> int:

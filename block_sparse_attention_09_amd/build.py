@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 SOURCES = ["msa_api.cpp", "index_score.hip", "index_score_tiled.hip", "topk.hip", "attn.hip",
-           "merge.hip", "gather.hip", "peaks.hip", "noalloc.hip"]
+           "merge.hip", "gather.hip", "peaks.hip", "noalloc.hip",
+           "decode_fused.hip"]
 ARCH = "gfx950"
 
 

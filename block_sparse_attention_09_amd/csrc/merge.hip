@@ -16,26 +16,17 @@
 // The output rows are stored non-temporally too: on the prefill shape, right
 // after the block-major kernel has written its 2.3 GB of partials, cached
 // stores cost 8 % more time than non-temporal ones.
+#include "merge_dev.h"
 #include "msa_internal.h"
 
 namespace msa {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// 16 lanes own one (row, head) pair, 8 dims (16 B) each; a workgroup of
-// THREADS threads serves THREADS / 16 pairs, consecutive heads.  Large merges
+// 16 lanes own one (row, head) pair (merge_pair16); a workgroup of THREADS
+// threads serves THREADS / 16 pairs, consecutive heads.  Large merges
 // (prefill) take 512 threads, so that the 32 heads' LSEs of one slot fill one
-// 128-byte line; small ones (decode) 256, for twice the workgroups.  Slots go in batches of kBatch (one batch holds a
-// top-16 + own selection) with every load of a batch -- the batch's LSEs and
-// all its partial rows -- issued before any is used, so a pair costs one
-// memory round trip per batch; batches are combined with a running maximum.
-// An empty slot (lse = -inf) gets weight 0 and its row is excluded by a
-// select, so whatever that row holds never reaches the result.
-constexpr int kBatch = 17;
-static_assert(kBatch == 17, "the LSE hand-round covers 16 lanes plus one");
+// 128-byte line; small ones (decode) 256, for twice the workgroups.
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void lse_merge_kernel(int64_t pairs, int H, int nslot,
                                                                   const bf16_t *__restrict__ o_part,
@@ -45,63 +36,7 @@ __global__ __launch_bounds__(THREADS) void lse_merge_kernel(int64_t pairs, int H
     const int64_t pair = (int64_t)blockIdx.x * (THREADS / 16) + (threadIdx.x >> 4);
     const int sub = threadIdx.x & 15;
     if (pair >= pairs) return;  // whole 16-lane groups leave together
-    // this pair's LSEs: lse_part [rows][nslot][H], slot s at ls[s * H]
-    const int64_t row = pair / H;
-    const float *ls = lse_part + row * nslot * H + (pair - row * H);
-    const bf16_t *op = o_part + pair * nslot * 128 + sub * 8;
-    float m = -INFINITY, wsum = 0.f;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s0 = 0; s0 < nslot; s0 += kBatch) {
-        float l[kBatch];
-        u32x4 v[kBatch];
-        // the batch's LSEs: one load per lane (lane sub holds slot s0 + sub, lane
-        // 0 also slot s0 + 16), handed round the 16 lanes of the pair
-        const float la = (s0 + sub < nslot)
-                             ? __builtin_nontemporal_load(ls + (int64_t)(s0 + sub) * H)
-                             : -INFINITY;
-        const float lb = (sub == 0 && s0 + 16 < nslot)
-                             ? __builtin_nontemporal_load(ls + (int64_t)(s0 + 16) * H)
-                             : -INFINITY;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const bool in = s0 + i < nslot;
-            l[i] = (i < 16) ? __shfl(la, i, 16) : __shfl(lb, 0, 16);
-            v[i] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                            op + (int64_t)(s0 + i) * 128))
-                      : u32x4{0u, 0u, 0u, 0u};
-        }
-        float mb = m;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) mb = fmaxf(mb, l[i]);
-        if (mb == -INFINITY) continue;  // nothing valid yet
-        const float rescale = __builtin_amdgcn_exp2f((m - mb) * kLog2e);  // 0 when m = -inf
-        wsum *= rescale;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= rescale;
-        m = mb;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const bool use = l[i] != -INFINITY;
-            const float w = use ? __builtin_amdgcn_exp2f((l[i] - m) * kLog2e) : 0.f;
-            wsum += w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += use ? w * bf16_lo(v[i][e]) : 0.f;
-                acc[2 * e + 1] += use ? w * bf16_hi(v[i][e]) : 0.f;
-            }
-        }
-    }
-    u32x4 out;
-    if (m == -INFINITY) {
-        out = u32x4{0u, 0u, 0u, 0u};
-    } else {
-        const float inv = 1.f / wsum;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    }
-    __builtin_nontemporal_store(out, reinterpret_cast<u32x4 *>(o + pair * 128 + sub * 8));
-    if (lse && sub == 0)
-        lse[pair] = (m == -INFINITY) ? -INFINITY : m + __builtin_amdgcn_logf(wsum) * kLn2;
+    merge_pair16(pair, H, nslot, o_part, lse_part, o, lse, sub);
 }
 
 }  // namespace

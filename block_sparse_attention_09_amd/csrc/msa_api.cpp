@@ -245,6 +245,27 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, int32_t rows, const 
     return hip_status(msa::launch_attn_decode(a, as_stream(stream)), "msa_sparse_attn_decode");
 }
 
+// Selection, page table and decode attention (validated arguments): one kernel
+// when its grid runs in a single round -- every workgroup repeats its group's
+// top-k, which costs nothing extra while all of them run at once but would be
+// paid again by every later round of a larger batch -- else top-k, then
+// attention.
+static hipError_t decode_select(const msa::AttnArgs &a, const float *scores, int32_t score_stride,
+                                int32_t k, const int32_t *row_req, const int32_t *block_table,
+                                int32_t bt_stride, int32_t *sel, int32_t *page_table,
+                                hipStream_t stream) {
+    const int64_t units = (int64_t)a.rows * a.G * a.nslot;
+    if (score_stride <= msa::kSelectMaxBlocks && units <= msa::decode_select_capacity(a.Hg)) {
+        const msa::SelectArgs sa{scores, score_stride, k,   row_req,
+                                 block_table, bt_stride, sel, page_table};
+        return msa::launch_attn_decode_select(a, sa, stream);
+    }
+    hipError_t e = msa::launch_topk(a.rows, a.G, scores, score_stride, a.row_pos, k, sel, stream,
+                                    row_req, block_table, bt_stride, page_table);
+    if (e == hipSuccess) e = msa::launch_attn_decode(a, stream);
+    return e;
+}
+
 msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
                                            const float *scores, int32_t score_stride, int32_t k,
                                            const int32_t *row_req, const int32_t *block_table,
@@ -266,21 +287,93 @@ msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
     REQUIRE(scores && block_table, MSA_ERR_NULL, "scores and block_table are required");
     const msa::AttnArgs a = attn_args(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
                                       sm_scale, o_part, lse_part);
-    // One kernel when its grid runs in a single round: every workgroup repeats
-    // its group's top-k, which costs nothing extra while all of them run at once
-    // but would be paid again by every later round of a larger batch.
-    const int64_t units = (int64_t)rows * dims->G * nslot;
-    if (score_stride <= msa::kSelectMaxBlocks && units <= msa::decode_select_capacity(dims->Hg)) {
-        const msa::SelectArgs sa{scores, score_stride, k,   row_req,
-                                 block_table, bt_stride, sel, page_table};
-        return hip_status(msa::launch_attn_decode_select(a, sa, as_stream(stream)),
-                          "msa_sparse_attn_decode_select");
+    return hip_status(decode_select(a, scores, score_stride, k, row_req, block_table, bt_stride,
+                                    sel, page_table, as_stream(stream)),
+                      "msa_sparse_attn_decode_select");
+}
+
+msa_status_t msa_decode_step(const msa_dims_t *dims, int32_t rows, const void *q_idx,
+                             msa_view_t k_idx, const int32_t *block_table, int32_t bt_stride,
+                             const int32_t *row_req, const int32_t *row_pos,
+                             const int32_t *blk_lo, int32_t num_reqs, int32_t score_stride,
+                             int32_t k, const void *q, msa_view_t kc, msa_view_t vc,
+                             float sm_scale, float *scores, int32_t *sel, int32_t *page_table,
+                             void *o_part, float *lse_part, void *o, float *lse, int32_t *sync,
+                             int32_t mode, msa_stream_t stream) {
+    msa_status_t st = check_dims(dims, true, true);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0, MSA_ERR_INVALID, "rows = %d must be >= 0", rows);
+    REQUIRE(mode == MSA_STEP_AUTO || mode == MSA_STEP_ONE_LAUNCH || mode == MSA_STEP_SEPARATE,
+            MSA_ERR_INVALID, "mode = %d: MSA_STEP_AUTO, MSA_STEP_ONE_LAUNCH or MSA_STEP_SEPARATE",
+            mode);
+    REQUIRE(score_stride >= 1, MSA_ERR_INVALID, "score_stride = %d must be >= 1", score_stride);
+    REQUIRE(bt_stride >= 1, MSA_ERR_INVALID, "bt_stride = %d must be >= 1", bt_stride);
+    REQUIRE(num_reqs >= 1, MSA_ERR_INVALID, "num_reqs = %d must be >= 1", num_reqs);
+    if ((st = check_k(k, rows, dims->G)) != MSA_OK) return st;
+    const int32_t nslot = k + 1;
+    st = check_attn(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos, sm_scale, o_part,
+                    lse_part);
+    if (st != MSA_OK) return st;
+    const bool supported = msa::decode_step_supported(dims->d_idx, score_stride);
+    REQUIRE(mode != MSA_STEP_ONE_LAUNCH || supported, MSA_ERR_UNSUPPORTED,
+            "MSA_STEP_ONE_LAUNCH needs score_stride <= %d", msa::kSelectMaxBlocks);
+    REQUIRE(mode != MSA_STEP_ONE_LAUNCH || sync, MSA_ERR_NULL,
+            "MSA_STEP_ONE_LAUNCH needs the sync words");
+    REQUIRE((int64_t)rows * dims->G < ((int64_t)1 << 28), MSA_ERR_INVALID,
+            "rows * G must be below 2^28");
+    if (rows == 0) return ok();
+    REQUIRE(q_idx && block_table && scores && o, MSA_ERR_NULL,
+            "q_idx, block_table, scores and o are required");
+    REQUIRE(aligned(q_idx, 16) && aligned(o, 16), MSA_ERR_INVALID,
+            "q_idx and o must be 16-byte aligned");
+    REQUIRE(aligned(scores, 4) && aligned(block_table, 4) && aligned(row_pos, 4) &&
+                aligned(sync, 4),
+            MSA_ERR_INVALID, "int32/fp32 arrays must be 4-byte aligned");
+    if ((st = check_view(k_idx, "k_idx")) != MSA_OK) return st;
+    // automatic choice: one launch for a decode batch (fewer than 64 rows per
+    // request: the shape msa_index_score scans with the streaming kernel) with
+    // few blocks to scan, when the sync words are given
+    const bool one =
+        supported && (mode == MSA_STEP_ONE_LAUNCH ||
+                      (mode == MSA_STEP_AUTO && sync &&
+                       (int64_t)rows * dims->G * score_stride <= msa::kStepAutoMaxBlocks &&
+                       (int64_t)rows < 64 * (int64_t)num_reqs));
+    const msa::AttnArgs a = attn_args(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
+                                      sm_scale, o_part, lse_part);
+    const hipStream_t s = as_stream(stream);
+    if (one) {
+        msa::StepArgs f{};
+        f.n_idx = dims->n_idx;
+        f.q_idx = static_cast<const msa::bf16_t *>(q_idx);
+        f.kidx = static_cast<const msa::bf16_t *>(k_idx.base);
+        f.kips = k_idx.page_stride;
+        f.kigs = k_idx.group_stride;
+        f.kits = k_idx.token_stride;
+        f.block_table = block_table;
+        f.bt_stride = bt_stride;
+        f.row_req = row_req;
+        f.blk_lo = blk_lo;
+        f.scores = scores;
+        f.score_stride = score_stride;
+        f.k = k;
+        f.sel = sel;
+        f.page_table = page_table;
+        f.o = static_cast<msa::bf16_t *>(o);
+        f.lse = lse;
+        f.index_scale = 1.0f / sqrtf((float)dims->d_idx);
+        f.sync = sync;
+        return hip_status(msa::launch_decode_step(a, f, dims->d_idx, s), "msa_decode_step");
     }
-    hipError_t e = msa::launch_topk(rows, dims->G, scores, score_stride, row_pos, k, sel,
-                                    as_stream(stream), row_req, block_table, bt_stride,
-                                    page_table);
-    if (e == hipSuccess) e = msa::launch_attn_decode(a, as_stream(stream));
-    return hip_status(e, "msa_sparse_attn_decode_select");
+    hipError_t e = msa::launch_index_score(*dims, rows, static_cast<const msa::bf16_t *>(q_idx),
+                                           k_idx, block_table, bt_stride, row_req, row_pos,
+                                           blk_lo, num_reqs, scores, score_stride, s);
+    if (e == hipSuccess)
+        e = decode_select(a, scores, score_stride, k, row_req, block_table, bt_stride, sel,
+                          page_table, s);
+    if (e == hipSuccess)
+        e = msa::launch_lse_merge(rows, dims->G * dims->Hg, nslot, a.o_part, lse_part,
+                                  static_cast<msa::bf16_t *>(o), lse, s);
+    return hip_status(e, "msa_decode_step");
 }
 
 msa_status_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t rows, int32_t nslot,

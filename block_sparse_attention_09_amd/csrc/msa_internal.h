@@ -54,6 +54,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
 // v combined with its value in lane l ^ mask, the result in every lane.  For
 // mask 16 and 32 the partner values come from the gfx950 lane-swap VALU ops
 // (v_permlane16_swap exchanges the odd 16-lane rows of one operand with the even
@@ -121,6 +124,26 @@ struct AttnArgs {
     float *lse_part;
 };
 
+// Index of the LSE of (row r, slot s, head h) in lse_part [rows][nslot][H]:
+// the heads of one (row, slot) are contiguous, so the Hg LSEs a (row, group,
+// slot) produces land in one sector instead of Hg scattered ones.
+__device__ __forceinline__ int64_t lse_index(const AttnArgs &a, int r, int s, int h) {
+    return ((int64_t)r * a.nslot + s) * (a.G * a.Hg) + h;
+}
+
+// o = 0, lse = -inf for the Hg heads of an empty (row, group, slot).
+template <int HG>
+__device__ __forceinline__ void write_empty_slot(const AttnArgs &a, int r, int g, int s, int tid,
+                                                 int nthreads) {
+    const int H = a.G * HG;
+    for (int i = tid; i < HG * 16; i += nthreads) {
+        const int hh = i >> 4, ch = i & 15;
+        const int64_t oi = ((int64_t)r * H + g * HG + hh) * a.nslot + s;
+        *reinterpret_cast<u32x4 *>(a.o_part + oi * 128 + ch * 8) = u32x4{0u, 0u, 0u, 0u};
+        if (ch == 0) a.lse_part[lse_index(a, r, s, g * HG + hh)] = -INFINITY;
+    }
+}
+
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
 
 // Top-k + page table + decode attention in one launch (sel, page_table written
@@ -137,6 +160,35 @@ struct SelectArgs {
 constexpr int kSelectMaxBlocks = 1024;
 hipError_t launch_attn_decode_select(const AttnArgs &a, const SelectArgs &sa, hipStream_t stream);
 int decode_select_capacity(int Hg);
+
+// The whole decode step in one launch (decode_fused.hip): the streaming scan,
+// selection, page table, slot partials and their merge, synchronised through
+// sync, int32 [kStepSyncHead + 2 * rows * G] (zero on entry, zero again when
+// the kernel ends; word 2 is set to 1 if a wait ever hit its poll bound).
+// a.sel / a.page_table are unused (f.sel / f.page_table are written).
+// Supported for d_idx 64 or 128 and score_stride <= kSelectMaxBlocks.
+struct StepArgs {
+    int n_idx;
+    const bf16_t *q_idx, *kidx;
+    int64_t kips, kigs, kits;
+    const int32_t *block_table;
+    int bt_stride;
+    const int32_t *row_req, *blk_lo;
+    float *scores;
+    int score_stride, k;
+    int32_t *sel, *page_table;
+    bf16_t *o;
+    float *lse;
+    float index_scale;  // 1 / sqrt(d_idx)
+    int32_t *sync;
+    int nscan_waves, spin_limit;  // set by launch_decode_step
+};
+constexpr int kStepSyncHead = 4;
+// msa_decode_step's automatic choice of the single launch: at most this many
+// scored blocks in the batch (a bound on the number of waves that fence)
+constexpr int64_t kStepAutoMaxBlocks = 4096;
+bool decode_step_supported(int d_idx, int score_stride);
+hipError_t launch_decode_step(const AttnArgs &a, StepArgs f, int d_idx, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int rows, int G, int nslot, int num_pages);
 

@@ -10,10 +10,12 @@
  * over only those blocks.  The six compute calls below are the steps of that
  * path: index scoring, top-k block selection, page-table build, sparse decode
  * attention, KV-block-major sparse prefill attention and the log-sum-exp merge.
- * Three more serve it: msa_topk_blocks_paged (selection and page table in one
+ * Four more serve it: msa_topk_blocks_paged (selection and page table in one
  * launch), msa_sparse_attn_decode_select (selection, page table and decode
- * attention in one launch) and msa_gather_pages (the selected KV pages of a
- * cache in host memory, loaded on demand into a device pool).
+ * attention in one launch), msa_decode_step (the whole decode step, one
+ * launch for short contexts and small batches) and msa_gather_pages (the
+ * selected KV pages of a cache in host memory, loaded on demand into a device
+ * pool).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -221,6 +223,60 @@ msa_status_t msa_sparse_attn_decode_select(const msa_dims_t *dims, int32_t rows,
                                            msa_view_t vc, const int32_t *row_pos, float sm_scale,
                                            int32_t *sel, int32_t *page_table, void *o_part,
                                            float *lse_part, msa_stream_t stream);
+
+/* ------------------------------------------------------------------ f1
+ * msa_decode_step -- the whole decode step: msa_index_score,
+ * msa_topk_blocks_paged, msa_sparse_attn_decode and msa_lse_merge.  Pages: the
+ * new smaller kernels of the path (the top-k among them) are named as fusion
+ * candidates (未来工作 of the aihot.news page); the steps are those of the
+ * decode index-scoring section (解码索引评分内核优化), the paged-attention
+ * integration (将 MSA 与分页注意力集成) and the log-sum-exp reduction of the
+ * per-block partials (KV 块主序稀疏注意力).
+ *
+ * Writes exactly what those calls write one after the other, bit for bit:
+ * scores (fp32 [rows][G][score_stride]), sel and page_table (int32
+ * [rows][G][k + 1]), o_part and lse_part (the slot partials), o (bf16
+ * [rows][G*Hg][128]) and lse (fp32 [rows][G*Hg], may be NULL).  Arguments as
+ * in those calls (nslot = k + 1; row_req and blk_lo may be NULL).  The one
+ * exception: MSA_STEP_ONE_LAUNCH always scores with the streaming scan that
+ * msa_index_score runs for decode batches; for batches of 64 or more rows per
+ * request msa_index_score takes its row-tiled matrix-core scan instead, whose
+ * scores agree with these to within rounding, not bit for bit.
+ *
+ *   sync  device int32 [MSA_DECODE_STEP_SYNC_WORDS(rows, G)], all zero before
+ *         its first use; every call leaves it zero again (a call that hits
+ *         the bound on its waits leaves word 2 set to 1: then the outputs are
+ *         not valid).  Calls that share one sync array must not overlap.
+ *         NULL is allowed with MSA_STEP_SEPARATE and MSA_STEP_AUTO (which then
+ *         runs the separate launches).
+ *   mode
+ *     MSA_STEP_ONE_LAUNCH  one kernel.  Its workgroups take tickets in the
+ *                          order they start: the first ones run the scan, the
+ *                          later ones one (row, group, slot) unit each, which
+ *                          waits for its pair's scan (only ever for workgroups
+ *                          that started before it, so every wait ends), then
+ *                          selects and attends; the last unit of a pair
+ *                          merges it.  Needs score_stride <= 1024
+ *                          (MSA_ERR_UNSUPPORTED otherwise) and sync.  The scan's
+ *                          waves each fence once per pair they finish, so this
+ *                          pays for short, small batches.
+ *     MSA_STEP_SEPARATE    the scan, then selection + attention
+ *                          (msa_sparse_attn_decode_select), then the merge.
+ *     MSA_STEP_AUTO        one launch when sync is given, rows * G *
+ *                          score_stride <= 4096 and there are fewer than 64
+ *                          rows per request; else separate.
+ * Errors: as the four calls; MSA_ERR_INVALID for an unknown mode or rows * G
+ * >= 2^28; MSA_ERR_NULL for MSA_STEP_ONE_LAUNCH without sync. */
+enum { MSA_STEP_AUTO = 0, MSA_STEP_ONE_LAUNCH = 1, MSA_STEP_SEPARATE = 2 };
+#define MSA_DECODE_STEP_SYNC_WORDS(rows, G) (4 + 2 * (int64_t)(rows) * (int64_t)(G))
+msa_status_t msa_decode_step(const msa_dims_t *dims, int32_t rows, const void *q_idx,
+                             msa_view_t k_idx, const int32_t *block_table, int32_t bt_stride,
+                             const int32_t *row_req, const int32_t *row_pos,
+                             const int32_t *blk_lo, int32_t num_reqs, int32_t score_stride,
+                             int32_t k, const void *q, msa_view_t kc, msa_view_t vc,
+                             float sm_scale, float *scores, int32_t *sel, int32_t *page_table,
+                             void *o_part, float *lse_part, void *o, float *lse, int32_t *sync,
+                             int32_t mode, msa_stream_t stream);
 
 /* ------------------------------------------------------------------ f4
  * msa_gather_pages -- on-demand load of the selected KV pages.

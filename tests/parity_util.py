@@ -73,6 +73,30 @@ def gpu_path(case, prefill=None, sel=None, pt=None, sm_scale=None):
             assert torch.equal(lse_d.view(torch.int32), lse_part.view(torch.int32)), \
                 "msa_sparse_attn_decode_select: lse_part differs"
     o, lse = msa.msa_lse_merge(o_part, lse_part)
+    if not prefill and sel is None and pt is None:
+        # the whole decode step in one call writes the same seven arrays, bit for
+        # bit, as separate launches and, where supported, as one kernel (whose
+        # scan is the streaming one: decode batches, fewer than 64 rows a request)
+        modes = [msa.MSA_STEP_SEPARATE, msa.MSA_STEP_AUTO]
+        if case.nb <= 1024 and case.rows < 64 * case.num_reqs:
+            modes += [msa.MSA_STEP_ONE_LAUNCH, msa.MSA_STEP_ONE_LAUNCH]  # twice: sync reuse
+        want = dict(scores=scores, sel=sel_gpu, pt=pt_gpu, o_part=o_part, lse_part=lse_part, o=o,
+                    lse=lse)
+        sync = torch.zeros(msa.decode_step_sync_words(case.rows, case.G), dtype=torch.int32,
+                           device=case.q.device)
+        for mode in modes:
+            got = dict(zip(want, msa.msa_decode_step(
+                d, case.q_idx, case.k_idx, case.block_table, case.row_pos, case.nb, case.k,
+                case.q, case.k_cache, case.v_cache, row_req=case.row_req, blk_lo=case.blk_lo,
+                num_reqs=case.num_reqs, sm_scale=scale, mode=mode, sync=sync)))
+            # the sync words are left zero (and no wait hit its bound)
+            assert int(torch.count_nonzero(sync)) == 0, f"msa_decode_step mode {mode}: sync words"
+            for key, ref in want.items():
+                same = torch.equal(got[key].contiguous().view(torch.int32 if ref.element_size() == 4
+                                                              else torch.int16),
+                                   ref.contiguous().view(torch.int32 if ref.element_size() == 4
+                                                         else torch.int16))
+                assert same, f"msa_decode_step mode {mode}: {key} differs"
     torch.cuda.synchronize()
     return {k: v.cpu() for k, v in dict(scores=scores, sel=sel_gpu, pt=pt_gpu, o_part=o_part,
                                         lse_part=lse_part, o=o, lse=lse).items()}

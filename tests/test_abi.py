@@ -174,6 +174,39 @@ def test_decode_select_validation(lib):
                           rp=None, o=None, lse=None) == MSA_OK
 
 
+def _decode_step(lib, dims, **kw):
+    a = dict(rows=1, qi=FAKE, ki=_view(), bt=FAKE, bts=4, rr=None, rp=FAKE, lo=None, nreq=1,
+             ss=4, k=2, q=FAKE, kc=_view(), vc=_view(), scale=0.088, scores=FAKE, sel=FAKE,
+             pt=FAKE, op=FAKE, lp=FAKE, o=FAKE, lse=None, sync=FAKE, mode=0)
+    a.update(kw)
+    return lib.msa_decode_step(
+        ctypes.byref(dims), a["rows"], a["qi"], a["ki"], a["bt"], a["bts"], a["rr"], a["rp"],
+        a["lo"], a["nreq"], a["ss"], a["k"], a["q"], a["kc"], a["vc"], a["scale"], a["scores"],
+        a["sel"], a["pt"], a["op"], a["lp"], a["o"], a["lse"], a["sync"], a["mode"], None)
+
+
+def test_decode_step_validation(lib):
+    assert _decode_step(lib, _dims(d_idx=96)) == MSA_ERR_UNSUPPORTED
+    assert _decode_step(lib, _dims(D=64)) == MSA_ERR_UNSUPPORTED
+    assert _decode_step(lib, _dims(), mode=3) == MSA_ERR_INVALID
+    assert b"mode" in lib.msa_last_error()
+    assert _decode_step(lib, _dims(), k=-1) == MSA_ERR_INVALID
+    assert _decode_step(lib, _dims(), ss=0) == MSA_ERR_INVALID
+    assert _decode_step(lib, _dims(), nreq=0) == MSA_ERR_INVALID
+    assert _decode_step(lib, _dims(), scale=0.0) == MSA_ERR_INVALID
+    assert _decode_step(lib, _dims(), qi=None) == MSA_ERR_NULL
+    assert _decode_step(lib, _dims(), scores=None) == MSA_ERR_NULL
+    assert _decode_step(lib, _dims(), o=None) == MSA_ERR_NULL
+    assert _decode_step(lib, _dims(), o=MISALIGNED) == MSA_ERR_INVALID
+    assert _decode_step(lib, _dims(), ki=_view(ts=100)) == MSA_ERR_INVALID
+    # the single launch: score rows of at most 1,024 blocks, and the sync words
+    assert _decode_step(lib, _dims(), ss=1025, mode=1) == MSA_ERR_UNSUPPORTED
+    assert _decode_step(lib, _dims(), sync=None, mode=1) == MSA_ERR_NULL
+    assert _decode_step(lib, _dims(), sync=MISALIGNED) == MSA_ERR_INVALID
+    assert _decode_step(lib, _dims(), rows=0, qi=None, bt=None, rp=None, q=None, scores=None,
+                        sel=None, pt=None, op=None, lp=None, o=None, sync=None) == MSA_OK
+
+
 def test_prefill_workspace(lib):
     d = _dims()
     n = ctypes.c_size_t(0)

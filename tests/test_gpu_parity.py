@@ -387,7 +387,7 @@ def test_empty_rows_is_noop():
     assert s.shape == (0, 2, case.nb)
 
 
-@pytest.mark.parametrize("form", ["decode", "decode-select", "prefill"])
+@pytest.mark.parametrize("form", ["decode", "decode-select", "decode-step", "prefill"])
 def test_graph_replay_matches_eager(form):
     """The step captured in a HIP graph (five calls, or three with the fused
     select + decode attention): every replay (with eager work and
@@ -410,8 +410,18 @@ def test_graph_replay_matches_eager(form):
     lse = torch.empty((case.rows, case.H), dtype=torch.float32, device=dev)
     ws = torch.empty(msa.msa_prefill_workspace_size(d, case.rows, case.nslot, case.num_pages),
                      dtype=torch.uint8, device=dev)
+    sync = torch.zeros(msa.decode_step_sync_words(case.rows, case.G), dtype=torch.int32,
+                       device=dev)
 
     def step():
+        if form == "decode-step":
+            # the whole step as one kernel, its sync words reused by every replay
+            msa.msa_decode_step(d, case.q_idx, case.k_idx, case.block_table, case.row_pos,
+                                case.nb, case.k, case.q, case.k_cache, case.v_cache,
+                                row_req=case.row_req, num_reqs=case.num_reqs,
+                                mode=msa.MSA_STEP_ONE_LAUNCH, sync=sync, scores=scores, sel=sel,
+                                page_table=pt, o_part=o_part, lse_part=lse_part, o=o, lse=lse)
+            return
         msa.msa_index_score(d, case.q_idx, case.k_idx, case.block_table, case.row_pos, case.nb,
                             row_req=case.row_req, num_reqs=case.num_reqs, scores=scores)
         if form == "decode-select":
@@ -455,5 +465,6 @@ def test_graph_replay_matches_eager(form):
         torch.cuda.synchronize()
         for a, b in zip((scores, sel, pt, o_part, lse_part, o, lse), ref):
             assert torch.equal(a, b), f"replay {rep} differs"
+        assert int(torch.count_nonzero(sync)) == 0, f"replay {rep}: sync words left set"
         step()  # eager work between replays
         torch.cuda.synchronize()
