@@ -258,6 +258,41 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
         b1.record()
         torch.cuda.synchronize()
         score_btb_ms = b0.elapsed_time(b1) / reps
+    # Prefill: attention and merge scheduled by query slabs
+    # (msa_sparse_attn_prefill_merged), each slab's partials merged right after
+    # its pass, against the whole batch as one slab.  Same output bit for bit.
+    slab_us = None
+    if case.prefill:
+        slab_us = {}
+        for div in (1, 2, 4, 8, 16, 32):
+            slab = max(1, case.rows // div)
+            nws = msa.msa_prefill_merged_workspace_size(d, case.rows, case.nslot, case.num_pages,
+                                                        slab)
+            wsm = torch.empty(nws, dtype=torch.uint8, device=dev)
+            om = torch.empty_like(o)
+            lm = torch.empty_like(lse)
+
+            def run_slabs():
+                msa.msa_sparse_attn_prefill_merged(d, case.q, case.k_cache, case.v_cache, sel, pt,
+                                                   case.row_pos, case.num_pages, scale,
+                                                   slab_rows=slab, workspace=wsm, o=om, lse=lm)
+            run_slabs()
+            torch.cuda.synchronize()
+            if not (torch.equal(om, o) and torch.equal(lm, lse)):
+                raise RuntimeError(f"{case.name}: slab {slab} output differs from the step")
+            ts = []
+            for _ in range(3):
+                flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run_slabs()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            slab_us[str(slab)] = round(min(ts), 1)
+            del wsm, om, lm
+        torch.cuda.empty_cache()
     per_fused = None
     if fused:
         for _ in range(warmup):
@@ -293,7 +328,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
         return case, dict(total_ms=eager_ms, ms_per_step=eager_ms / steps, eager_ms=eager_ms,
                           eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
                           per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu(),
-                          score_btb_ms=score_btb_ms)
+                          score_btb_ms=score_btb_ms, slab_us=slab_us)
 
     # The same step captured once in a HIP graph and replayed: removes the
     # host launch gaps between the calls.  Every replay must reproduce the
@@ -340,7 +375,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
                       eager_ms_per_step=eager_ms / steps, graph_ms_per_step=graph_ms / steps,
                       wall_s=wall, per_call_ms=per, per_call_fused_ms=per_fused,
                       step_pct_ms=pct, alg=alg, sel=sel.cpu(), warm_ms_per_step=warm_ms / steps,
-                      score_btb_ms=score_btb_ms)
+                      score_btb_ms=score_btb_ms, slab_us=slab_us)
 
 
 def traffic_from_profile():
@@ -541,6 +576,10 @@ def summarize(cfg, case, r, peaks=None):
             res["attn_frac_of_random_operand_mfma"] = round(
                 res["attn_tflops_kernel_call"] / peaks["mfma_bf16_random_TFLOPs"], 4)
         res["attn_flops"] = a["attn_flops"]
+        if r.get("slab_us"):
+            # msa_sparse_attn_prefill_merged by slab size (rows per slab): the
+            # block-major attention and the merge, partials slab by slab
+            res["attn_merge_by_slab_us"] = r["slab_us"]
         # index scoring contracts qbar = sum_j q_j (one vector per (row, group))
         # with the visible key-index tokens: 2 d_idx FLOP per token, reported as
         # index_qbar_tflops; the matrix cores take qbar as bf16 hi + lo, two

@@ -9,8 +9,10 @@ the first call raises.
 Calls (same names and meaning as the C functions):
     msa_index_score, msa_topk_blocks, msa_build_page_table, msa_topk_blocks_paged,
     msa_sparse_attn_decode, msa_sparse_attn_decode_select, msa_decode_step,
+    msa_prefill_merged_workspace_size,
     msa_prefill_workspace_size,
-    msa_sparse_attn_prefill, msa_sparse_attn_prefill_noalloc,
+    msa_sparse_attn_prefill, msa_sparse_attn_prefill_noalloc, msa_sparse_attn_prefill_merged,
+    msa_prefill_merged_workspace_size,
     msa_lse_merge, msa_version, msa_gather_pages
 Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout);
 MSA_STEP_AUTO, MSA_STEP_ONE_LAUNCH, MSA_STEP_SEPARATE (msa_decode_step modes),
@@ -37,10 +39,12 @@ from .binding import (  # noqa: F401
     msa_peak_mfma_bf16,
     msa_peak_mfma_bf16_random,
     msa_peak_stream_read,
+    msa_prefill_merged_workspace_size,
     msa_prefill_workspace_size,
     msa_sparse_attn_decode,
     msa_sparse_attn_decode_select,
     msa_sparse_attn_prefill,
+    msa_sparse_attn_prefill_merged,
     msa_sparse_attn_prefill_noalloc,
     msa_topk_blocks,
     msa_topk_blocks_paged,

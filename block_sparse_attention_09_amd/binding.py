@@ -54,6 +54,10 @@ _SIGS = {
     "msa_decode_step": [_DIMS, _I32, _P, View, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, View,
                         View, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "msa_prefill_workspace_size": [_DIMS, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "msa_prefill_merged_workspace_size": [_DIMS, _I32, _I32, _I32, _I32,
+                                          ctypes.POINTER(ctypes.c_size_t)],
+    "msa_sparse_attn_prefill_merged": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
+                                       ctypes.c_float, _I32, _P, ctypes.c_size_t, _P, _P, _P],
     "msa_sparse_attn_prefill": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
                                 ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
     "msa_sparse_attn_prefill_noalloc": [_DIMS, _I32, _P, View, View, _P, _P, _I32, _P, _I32,
@@ -332,6 +336,39 @@ def msa_decode_step(dims: Dims, q_idx, k_idx, block_table, row_pos, score_stride
         _ptr(lse_part), _ptr(o), _ptr(lse), _ptr(sync), int(mode), _stream(stream)),
         "msa_decode_step")
     return scores, sel, page_table, o_part, lse_part, o, lse
+
+
+def msa_prefill_merged_workspace_size(dims: Dims, rows, nslot, num_pages, slab_rows=0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().msa_prefill_merged_workspace_size(ctypes.byref(dims), rows, nslot, num_pages,
+                                                    slab_rows, ctypes.byref(n)),
+           "msa_prefill_merged_workspace_size")
+    return n.value
+
+
+def msa_sparse_attn_prefill_merged(dims: Dims, q, k_cache, v_cache, sel, page_table, row_pos,
+                                   num_pages, sm_scale=None, slab_rows=0, workspace=None, o=None,
+                                   lse=None, stream=None):
+    """Block-major prefill attention and its merge by query slabs; returns (o, lse)."""
+    _need(q, torch.bfloat16, "q", True)
+    _i32(sel, "sel"), _i32(page_table, "page_table"), _i32(row_pos, "row_pos")
+    rows, H, D = q.shape
+    nslot = sel.shape[2]
+    need = msa_prefill_merged_workspace_size(dims, rows, nslot, num_pages, slab_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((rows, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((rows, H), dtype=torch.float32, device=q.device)
+    scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dims.D))
+    kv = view_of(k_cache, host_ok=True), view_of(v_cache, host_ok=True)
+    _check(load().msa_sparse_attn_prefill_merged(
+        ctypes.byref(dims), rows, _ptr(q), kv[0], kv[1], _ptr(sel), _ptr(page_table), nslot,
+        _ptr(row_pos), num_pages, scale, int(slab_rows), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(o), _ptr(lse), _stream(stream)),
+        "msa_sparse_attn_prefill_merged")
+    return o, lse
 
 
 def msa_prefill_workspace_size(dims: Dims, rows, nslot, num_pages) -> int:

@@ -3,6 +3,7 @@
 // allocates; every kernel goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -436,6 +437,80 @@ msa_status_t msa_sparse_attn_prefill_noalloc(const msa_dims_t *dims, int32_t row
         attn_args(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale, o_part, lse_part);
     return hip_status(msa::launch_attn_prefill(a, num_pages, ws, as_stream(stream)),
                       "msa_sparse_attn_prefill_noalloc");
+}
+
+// Workspace of the slab-scheduled prefill: the remap of one slab, then the
+// slab's partial outputs and LSEs.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+struct SlabLayout {
+    size_t remap, part, lse, total;
+};
+static SlabLayout slab_layout(const msa_dims_t *d, int32_t slab, int32_t nslot, int32_t num_pages) {
+    SlabLayout L;
+    const size_t H = (size_t)d->G * d->Hg;
+    L.remap = align256(msa::prefill_workspace_bytes(slab, d->G, nslot, num_pages));
+    L.part = align256((size_t)slab * H * nslot * 128 * sizeof(uint16_t));
+    L.lse = align256((size_t)slab * H * nslot * sizeof(float));
+    L.total = L.remap + L.part + L.lse;
+    return L;
+}
+
+msa_status_t msa_prefill_merged_workspace_size(const msa_dims_t *dims, int32_t rows,
+                                               int32_t nslot, int32_t num_pages,
+                                               int32_t slab_rows, size_t *bytes) {
+    REQUIRE(bytes, MSA_ERR_NULL, "bytes is NULL");
+    msa_status_t st = check_dims(dims, false, true);
+    if (st != MSA_OK) return st;
+    REQUIRE(rows >= 0 && nslot >= 1 && num_pages >= 1 && slab_rows >= 0, MSA_ERR_INVALID,
+            "rows >= 0, nslot >= 1, num_pages >= 1 and slab_rows >= 0 are required");
+    const int32_t slab = (slab_rows == 0 || slab_rows > rows) ? rows : slab_rows;
+    *bytes = slab_layout(dims, slab, nslot, num_pages).total;
+    return ok();
+}
+
+msa_status_t msa_sparse_attn_prefill_merged(const msa_dims_t *dims, int32_t rows, const void *q,
+                                            msa_view_t k, msa_view_t v, const int32_t *sel,
+                                            const int32_t *page_table, int32_t nslot,
+                                            const int32_t *row_pos, int32_t num_pages,
+                                            float sm_scale, int32_t slab_rows, void *workspace,
+                                            size_t workspace_bytes, void *o, float *lse,
+                                            msa_stream_t stream) {
+    // the partials live in the workspace: check_attn's o_part / lse_part
+    // requirements are met by the workspace checks below
+    msa_status_t st = check_attn(dims, rows, q, k, v, sel, page_table, nslot, row_pos, sm_scale,
+                                 workspace, static_cast<const float *>(workspace));
+    if (st != MSA_OK) return st;
+    REQUIRE(num_pages >= 1, MSA_ERR_INVALID, "num_pages = %d must be >= 1", num_pages);
+    REQUIRE((int64_t)dims->G * num_pages < ((int64_t)1 << 31) - 1, MSA_ERR_INVALID,
+            "G * num_pages must fit in int32");
+    REQUIRE(slab_rows >= 0, MSA_ERR_INVALID, "slab_rows = %d must be >= 0", slab_rows);
+    if (rows == 0) return ok();
+    REQUIRE(o, MSA_ERR_NULL, "o is required");
+    REQUIRE(aligned(o, 16), MSA_ERR_INVALID, "o must be 16-byte aligned");
+    const int32_t slab = (slab_rows == 0 || slab_rows > rows) ? rows : slab_rows;
+    const SlabLayout L = slab_layout(dims, slab, nslot, num_pages);
+    REQUIRE(aligned(workspace, 256), MSA_ERR_INVALID, "workspace must be 256-byte aligned");
+    REQUIRE(workspace_bytes >= L.total, MSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu",
+            workspace_bytes, L.total);
+    char *ws = static_cast<char *>(workspace);
+    void *part = ws + L.remap;
+    float *lse_part = reinterpret_cast<float *>(ws + L.remap + L.part);
+    const int H = dims->G * dims->Hg;
+    const hipStream_t s = as_stream(stream);
+    for (int32_t r0 = 0; r0 < rows; r0 += slab) {
+        const int32_t n = std::min(slab, rows - r0);
+        const size_t sl = (size_t)r0 * dims->G * nslot;
+        const msa::AttnArgs a = attn_args(
+            dims, n, static_cast<const msa::bf16_t *>(q) + (size_t)r0 * H * 128, k, v, sel + sl,
+            page_table + sl, nslot, row_pos + r0, sm_scale, part, lse_part);
+        hipError_t e = msa::launch_attn_prefill(a, num_pages, ws, s);
+        if (e == hipSuccess)
+            e = msa::launch_lse_merge(n, H, nslot, static_cast<const msa::bf16_t *>(part),
+                                      lse_part, static_cast<msa::bf16_t *>(o) + (size_t)r0 * H * 128,
+                                      lse ? lse + (size_t)r0 * H : nullptr, s);
+        if (e != hipSuccess) return hip_status(e, "msa_sparse_attn_prefill_merged");
+    }
+    return ok();
 }
 
 msa_status_t msa_lse_merge(int32_t rows, int32_t H, int32_t nslot, int32_t D, const void *o_part,

@@ -326,6 +326,40 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t rows, const
                                      void *workspace, size_t workspace_bytes, void *o_part,
                                      float *lse_part, msa_stream_t stream);
 
+/* ------------------------------------------------------------------ f3
+ * msa_sparse_attn_prefill_merged -- msa_sparse_attn_prefill and msa_lse_merge
+ * scheduled by query slabs.  Pages: KV-block-major section (KV 块主序稀疏注意力:
+ * per-block partial outputs combined by a log-sum-exp reduction) and the fusion
+ * of the q->kv remap named in 未来工作 of the aihot.news page.
+ *
+ * The rows are taken in slabs of slab_rows (0: all rows in one slab); for each
+ * slab the q->kv inversion, the block-major attention and the merge run one
+ * after the other, the slab's partials in the workspace, so the partials of a
+ * slab are read back by its merge right after they are written (while they may
+ * still sit in L2 / the last-level cache) and the caller never holds
+ * rows x H x nslot partials.  Writes o (bf16 [rows][G*Hg][128], 16-byte aligned)
+ * and lse (fp32 [rows][G*Hg], may be NULL): bit for bit what
+ * msa_sparse_attn_prefill followed by msa_lse_merge write, for every slab size
+ * (a partial depends only on its own row).  Smaller slabs hold fewer partials
+ * but load each selected KV block once per slab that selects it.
+ *
+ *   slab_rows   >= 0; rows per slab (0 or >= rows: one slab)
+ *   workspace   device buffer of at least msa_prefill_merged_workspace_size()
+ *               bytes (same slab_rows), 256-byte aligned; contents ignored
+ * Other arguments as msa_sparse_attn_prefill.  Errors: as that call;
+ * MSA_ERR_WORKSPACE for a workspace smaller than needed. */
+msa_status_t msa_prefill_merged_workspace_size(const msa_dims_t *dims, int32_t rows,
+                                               int32_t nslot, int32_t num_pages,
+                                               int32_t slab_rows, size_t *bytes);
+
+msa_status_t msa_sparse_attn_prefill_merged(const msa_dims_t *dims, int32_t rows, const void *q,
+                                            msa_view_t k, msa_view_t v, const int32_t *sel,
+                                            const int32_t *page_table, int32_t nslot,
+                                            const int32_t *row_pos, int32_t num_pages,
+                                            float sm_scale, int32_t slab_rows, void *workspace,
+                                            size_t workspace_bytes, void *o, float *lse,
+                                            msa_stream_t stream);
+
 /* ------------------------------------------------------------------ a8 / a9, no allocation
  * msa_sparse_attn_prefill_noalloc -- msa_sparse_attn_prefill for callers that
  * cannot allocate device memory (code under HIP graph capture, serving loops

@@ -73,6 +73,17 @@ def gpu_path(case, prefill=None, sel=None, pt=None, sm_scale=None):
             assert torch.equal(lse_d.view(torch.int32), lse_part.view(torch.int32)), \
                 "msa_sparse_attn_decode_select: lse_part differs"
     o, lse = msa.msa_lse_merge(o_part, lse_part)
+    if prefill:
+        # the slab-scheduled prefill (inversion, attention and merge per slab of
+        # rows) writes the same output and LSE, bit for bit, for any slab size
+        for slab in (0, 97, max(1, case.rows // 3)):
+            o_m, lse_m = msa.msa_sparse_attn_prefill_merged(
+                d, case.q, case.k_cache, case.v_cache, use_sel, use_pt, case.row_pos,
+                case.num_pages, scale, slab_rows=slab)
+            assert torch.equal(o_m.view(torch.int16), o.view(torch.int16)), \
+                f"msa_sparse_attn_prefill_merged slab {slab}: o differs"
+            assert torch.equal(lse_m.view(torch.int32), lse.view(torch.int32)), \
+                f"msa_sparse_attn_prefill_merged slab {slab}: lse differs"
     if not prefill and sel is None and pt is None:
         # the whole decode step in one call writes the same seven arrays, bit for
         # bit, as separate launches and, where supported, as one kernel (whose

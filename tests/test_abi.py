@@ -207,6 +207,36 @@ def test_decode_step_validation(lib):
                         sel=None, pt=None, op=None, lp=None, o=None, sync=None) == MSA_OK
 
 
+def test_prefill_merged_validation(lib):
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    sizes = []
+    for slab in (0, 8192, 4096, 1024, 1):
+        assert lib.msa_prefill_merged_workspace_size(ctypes.byref(d), 8192, 17, 544, slab,
+                                                     ctypes.byref(n)) == MSA_OK
+        sizes.append(n.value)
+    # one slab of all rows holds every partial; smaller slabs need less
+    assert sizes[0] == sizes[1] > sizes[2] > sizes[3] > sizes[4]
+    assert sizes[0] >= 8192 * 64 * 17 * (128 * 2 + 4)
+    assert lib.msa_prefill_merged_workspace_size(ctypes.byref(d), 8192, 17, 544, -1,
+                                                 ctypes.byref(n)) == MSA_ERR_INVALID
+    need = sizes[2]
+
+    def call(**kw):
+        a = dict(rows=8192, slab=4096, ws=FAKE, wsb=need, o=FAKE, q=FAKE)
+        a.update(kw)
+        return lib.msa_sparse_attn_prefill_merged(
+            ctypes.byref(d), a["rows"], a["q"], _view(), _view(), FAKE, FAKE, 17, FAKE, 544,
+            0.088, a["slab"], a["ws"], a["wsb"], a["o"], None, None)
+    assert call(wsb=need - 1) == MSA_ERR_WORKSPACE
+    assert call(slab=-1) == MSA_ERR_INVALID
+    assert call(o=None) == MSA_ERR_NULL
+    assert call(o=MISALIGNED) == MSA_ERR_INVALID
+    assert call(ws=ctypes.c_void_p(0x10010)) == MSA_ERR_INVALID      # not 256-byte aligned
+    assert call(ws=None) == MSA_ERR_NULL
+    assert call(rows=0, ws=None, o=None, q=None) == MSA_OK
+
+
 def test_prefill_workspace(lib):
     d = _dims()
     n = ctypes.c_size_t(0)
