@@ -45,7 +45,9 @@ BF16_PEAK_TFLOPS = 2500.0
 FLUSH_BYTES = 1 << 30
 MAIN = 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_decode-64k-b8.json")
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc", "index_score.hip")
+# the index-score kernel's sources (the counter summary names their hash)
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc", f)
+               for f in ("index_score.hip", "index_score_dev.h")]
 
 
 def parse():
@@ -385,7 +387,7 @@ def traffic_from_profile():
         info = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SRCS)).hexdigest()[:16]
     if info.get("kernel_source_sha256_16") != src_hash:
         return None
     return info.get("hbm_bytes_per_launch")
