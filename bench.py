@@ -518,7 +518,28 @@ def measured_peaks():
         return min(out)
 
     t_read = best(lambda: msa.msa_peak_stream_read(buf, sink), 5)
-    del buf
+    # write, then read the same bytes back right away (after a 1 GiB read that
+    # leaves the caches cold): below the 256 MB last-level cache the read can
+    # find them there
+    flush = buf[: (1 << 30) // 4]
+    wb = {}
+    for label, n in (("144MiB", 144 << 20), ("2GiB", 2 << 30)):
+        tgt = buf[(1 << 30) // 4:(1 << 30) // 4 + n // 4]
+        tw, tr = [], []
+        for rep in range(3):
+            msa.msa_peak_stream_read(flush, sink)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            msa.msa_peak_stream_write(tgt, rep)
+            e[1].record()
+            msa.msa_peak_stream_read(tgt, sink)
+            e[2].record()
+            torch.cuda.synchronize()
+            tw.append(e[0].elapsed_time(e[1]))
+            tr.append(e[1].elapsed_time(e[2]))
+        wb[label] = dict(write_GBps=round(n / (min(tw) * 1e-3) / 1e9, 1),
+                         read_back_GBps=round(n / (min(tr) * 1e-3) / 1e9, 1))
+    del buf, flush
     torch.cuda.empty_cache()
     iters = 16384
     flops = msa.msa_peak_mfma_bf16(iters, sink)
@@ -529,12 +550,15 @@ def measured_peaks():
     return dict(stream_read_GBps=round(nbytes / (t_read * 1e-3) / 1e9, 1),
                 mfma_bf16_TFLOPs=round(flops / (t_mfma * 1e-3) / 1e12, 1),
                 mfma_bf16_random_TFLOPs=round(flops_r / (t_mfma_r * 1e-3) / 1e12, 1),
+                write_then_read_back=wb,
                 method=("msa_peak_stream_read over 4 GiB (a workgroup per 64 KB chunk, 8 "
                         "non-temporal 16-B loads in flight per thread); msa_peak_mfma_bf16: 4 "
                         "independent 32x32x16 bf16 MFMA chains per wave on fixed operands, 2 "
                         "waves per SIMD; msa_peak_mfma_bf16_random: the same on pseudo-random "
                         "unit-variance operands (the matrix cores' rate depends on the data); "
-                        "best of 5, 3 and 3 launches"))
+                        "best of 5, 3 and 3 launches; write_then_read_back: msa_peak_stream_write "
+                        "of 144 MiB / 2 GiB after a 1 GiB cache-clearing read, then "
+                        "msa_peak_stream_read of the same bytes, best of 3"))
 
 
 def summarize(cfg, case, r, peaks=None):

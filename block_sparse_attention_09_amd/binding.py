@@ -65,6 +65,7 @@ _SIGS = {
     "msa_lse_merge": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     "msa_gather_pages": [_DIMS, _I32, _P, _I32, View, View, _P, _P, _P, _P],
     "msa_peak_stream_read": [_P, ctypes.c_size_t, _P, _P],
+    "msa_peak_stream_write": [_P, ctypes.c_size_t, ctypes.c_uint32, _P],
     "msa_peak_mfma_bf16": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
     "msa_peak_mfma_bf16_random": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
 }
@@ -466,6 +467,15 @@ def msa_peak_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     _need(sink, torch.float32, "sink")
     _check(load().msa_peak_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                        _stream(stream)), "msa_peak_stream_read")
+
+
+def msa_peak_stream_write(buf: torch.Tensor, tag: int = 0, stream=None):
+    """Launch the streaming-write probe over every byte of `buf` (include/msa_peaks.h)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(load().msa_peak_stream_write(_ptr(buf), buf.numel() * buf.element_size(),
+                                        int(tag) & 0xffffffff, _stream(stream)),
+           "msa_peak_stream_write")
 
 
 def msa_peak_mfma_bf16(iters: int, sink: torch.Tensor, stream=None) -> float:

@@ -560,6 +560,15 @@ msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
                       "msa_peak_stream_read");
 }
 
+msa_status_t msa_peak_stream_write(void *buf, size_t bytes, uint32_t tag, msa_stream_t stream) {
+    REQUIRE(bytes % 16 == 0, MSA_ERR_INVALID, "bytes = %zu must be a multiple of 16", bytes);
+    if (bytes == 0) return ok();
+    REQUIRE(buf, MSA_ERR_NULL, "buf is required");
+    REQUIRE(aligned(buf, 16), MSA_ERR_INVALID, "buf must be 16-byte aligned");
+    return hip_status(msa::launch_peak_stream_write(buf, (int64_t)bytes, tag, as_stream(stream)),
+                      "msa_peak_stream_write");
+}
+
 msa_status_t msa_peak_mfma_bf16(int32_t iters, float *sink, double *flops, msa_stream_t stream) {
     REQUIRE(iters >= 1, MSA_ERR_INVALID, "iters = %d must be >= 1", iters);
     REQUIRE(sink && flops, MSA_ERR_NULL, "sink and flops are required");

@@ -211,6 +211,7 @@ hipError_t launch_gather_pages(int rows, int G, int nslot, const int32_t *page_t
 // measured-peak probes (not part of the MSA path)
 hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
                                    hipStream_t stream);
+hipError_t launch_peak_stream_write(void *buf, int64_t bytes, uint32_t tag, hipStream_t stream);
 hipError_t launch_peak_mfma_bf16(int iters, float *sink, double *flops, hipStream_t stream);
 hipError_t launch_peak_mfma_bf16_random(int iters, float *sink, double *flops,
                                        hipStream_t stream);

@@ -1,6 +1,7 @@
 // peaks.hip -- measured machine peaks (gfx950), the reference points the MSA
 // kernels' rooflines are read against besides the published ones: a plain
-// streaming read of a large buffer (HBM) and register-resident bf16 MFMA loops
+// streaming read of a large buffer (HBM), a streaming write (whose bytes a read
+// right after may find in the last-level cache) and register-resident bf16 MFMA loops
 // (matrix cores), one on fixed low-entropy operands and one on pseudo-random
 // operands of unit variance like the MSA workloads' values: the matrix cores'
 // sustained rate depends on the operand bits they toggle (the chip lowers its
@@ -42,6 +43,19 @@ __global__ __launch_bounds__(kPeakThreads) void stream_read_kernel(const u32x4 *
         acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
     }
     if (acc == 0x9e3779b9u) sink[0] = __uint_as_float(acc);
+}
+
+// Streaming write of the same shape: workgroup w writes its 64 KB chunk, every
+// thread storing eight 16-B values per round (cached stores, so a read of the
+// same bytes right after can find them in the last-level cache).
+__global__ __launch_bounds__(kPeakThreads) void stream_write_kernel(u32x4 *__restrict__ p,
+                                                                    int64_t n16, uint32_t tag) {
+    const int64_t b = (int64_t)blockIdx.x * kReadChunk16;
+    const int64_t e = b + kReadChunk16 < n16 ? b + kReadChunk16 : n16;
+    for (int64_t i = b + threadIdx.x; i < e; i += kPeakThreads) {
+        const uint32_t x = tag ^ (uint32_t)i;
+        p[i] = u32x4{x, x + 1u, x + 2u, x + 3u};
+    }
 }
 
 // Four independent 32x32x16 bf16 accumulation chains per wave, operands in
@@ -117,6 +131,14 @@ hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
     const int64_t grid = (n16 + kReadChunk16 - 1) / kReadChunk16;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kPeakThreads), 0, stream,
                        static_cast<const u32x4 *>(buf), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_peak_stream_write(void *buf, int64_t bytes, uint32_t tag, hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    const int64_t grid = (n16 + kReadChunk16 - 1) / kReadChunk16;
+    hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)grid), dim3(kPeakThreads), 0, stream,
+                       static_cast<u32x4 *>(buf), n16, tag);
     return hipGetLastError();
 }
 

@@ -27,6 +27,15 @@ extern "C" {
 msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
                                   msa_stream_t stream);
 
+/* Streaming write of `bytes` bytes at `buf` (device, 16-byte aligned, bytes a
+ * multiple of 16), every 16-byte unit i set to a value made of tag ^ i, one
+ * 256-thread workgroup per 64 KB chunk, cached stores.  Time it with events for
+ * the write rate; time msa_peak_stream_read of the same bytes right after it
+ * (caches otherwise cold) for the rate at which freshly written data reads
+ * back from the last-level cache (sizes below its 256 MB) or from HBM.
+ * Errors: MSA_ERR_INVALID (alignment, size), MSA_ERR_NULL, MSA_ERR_HIP. */
+msa_status_t msa_peak_stream_write(void *buf, size_t bytes, uint32_t tag, msa_stream_t stream);
+
 /* Register-resident bf16 matrix-core loop: two 256-thread workgroups per CU,
  * each wave runs `iters` iterations of four independent 32x32x16 bf16 MFMA
  * accumulation chains.  *flops (host) receives the floating-point operations the

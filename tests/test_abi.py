@@ -288,6 +288,10 @@ def test_peak_probe_validation(lib):
     assert lib.msa_peak_mfma_bf16(0, FAKE, ctypes.byref(flops), None) == MSA_ERR_INVALID
     assert lib.msa_peak_mfma_bf16(8, None, ctypes.byref(flops), None) == MSA_ERR_NULL
     assert lib.msa_peak_mfma_bf16(8, FAKE, None, None) == MSA_ERR_NULL
+    assert lib.msa_peak_stream_write(FAKE, 24, 0, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_stream_write(MISALIGNED, 32, 0, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_stream_write(None, 32, 0, None) == MSA_ERR_NULL
+    assert lib.msa_peak_stream_write(None, 0, 0, None) == MSA_OK
     assert lib.msa_peak_mfma_bf16_random(0, FAKE, ctypes.byref(flops), None) == MSA_ERR_INVALID
     assert lib.msa_peak_mfma_bf16_random(8, None, ctypes.byref(flops), None) == MSA_ERR_NULL
 

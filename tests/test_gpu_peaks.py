@@ -44,3 +44,27 @@ def test_mfma_probe():
     ms = _time(lambda: msa.msa_peak_mfma_bf16(iters, sink))
     tflops = flops / (ms * 1e-3) / 1e12
     assert 200.0 < tflops < 2600.0, tflops
+
+
+def test_stream_write_probe():
+    """Every 16-byte unit i holds (tag ^ i) + 0, 1, 2, 3, including a ragged last chunk."""
+    n16 = (64 << 10) // 16 * 5 + 37
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device="cuda")
+    tag = 0x5A5A1234
+    msa.msa_peak_stream_write(buf, tag)
+    got = buf.view(n16, 4).cpu().to(torch.int64) & 0xFFFFFFFF
+    i = torch.arange(n16, dtype=torch.int64)
+    x = (i ^ tag) & 0xFFFFFFFF
+    want = torch.stack([(x + j) & 0xFFFFFFFF for j in range(4)], dim=1)
+    assert torch.equal(got, want)
+
+
+def test_random_operand_mfma_probe():
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    iters = 512
+    flops = msa.msa_peak_mfma_bf16_random(iters, sink)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == 2 * cus * 4 * iters * 16 * (2 * 32 * 32 * 16)
+    ms = _time(lambda: msa.msa_peak_mfma_bf16_random(iters, sink))
+    tflops = flops / (ms * 1e-3) / 1e12
+    assert 200.0 < tflops < 2600.0, tflops
