@@ -83,16 +83,19 @@ __device__ __forceinline__ void stage_kv_load(KvStage &st, const bf16_t *kp, int
     }
 }
 
-// Writes the staged tiles; V rows of tokens past last_tok (seen by no query
-// of the unit, possibly never written) are stored as zeros, since a zero
-// softmax weight times a non-finite cache value would still poison P V.
+// Writes the staged tiles; K and V rows of tokens past last_tok (seen by no
+// query of the unit, possibly never written) are stored as zeros: a zero
+// softmax weight times a non-finite V value would still poison P V, and the
+// masked scores start from -inf (blockmajor_wave), which a non-finite K row
+// would turn into NaN.
 __device__ __forceinline__ void stage_kv_store(AttnSmem &sm, const KvStage &st, int last_tok) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = tid + kAttnThreads * i;
         const int t = c >> 4, d0 = (c & 15) * 8;
-        *reinterpret_cast<u32x4 *>(&sm.k[t * KST + d0]) = st.kw[i];
+        *reinterpret_cast<u32x4 *>(&sm.k[t * KST + d0]) =
+            (t <= last_tok) ? st.kw[i] : u32x4{0u, 0u, 0u, 0u};
         const u32x4 v = (t <= last_tok) ? st.vw[i] : u32x4{0u, 0u, 0u, 0u};
         bf16_t *col = &sm.vt[d0 * KST + vt_col(t)];
 #pragma unroll
@@ -178,15 +181,44 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
         // loads and stores in the gaps instead of delaying them (3 % on the 8K
         // prefill chunk)
         __builtin_amdgcn_s_setprio(1);
-        // S^T = K Q^T: four 32-token row tiles, 8 dimension steps of 16
+        // S^T = K Q^T: four 32-token row tiles, 8 dimension steps of 16.  The
+        // causal mask lives in the accumulators' initial values: element 4 q + r
+        // of s[mt] (token 32 mt + 8 q + 4 h + r) starts at 0 if the row sees the
+        // token and at -inf if not, so the product leaves masked scores at -inf
+        // and the softmax below needs no branch (a select after the product would
+        // redefine the accumulators and cost a copy of all 64 per tile).  The
+        // decision is an integer sign mask: -inf's bits where 32 mt + 8 q + r >
+        // vis - 4 h.  K rows no query of the unit sees are zero (stage_kv_store),
+        // so every masked product stays -inf.  Tiles whose rows all see the whole
+        // block start from zero.
+        const int vis = meta.valid ? meta.pos - meta.blk * kBlk : -1;
         f32x16 s[4];
+        // the product runs in each branch, so that both define the accumulators
+        // from their initial values (zero as the MFMA's inline operand on the
+        // common, unmasked path)
+        auto qk = [&]() {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) s[mt] = f32x16{};
+            for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+                for (int mt = 0; mt < 4; ++mt)
+                    s[mt] = mfma32(lds16(&sm.k[(32 * mt + j) * KST + 16 * ks + 8 * h]), qb[ks],
+                                   s[mt]);
+        };
+        if (__builtin_amdgcn_readfirstlane(__all(vis >= kBlk - 1))) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) s[mt] = f32x16{};
+            qk();
+        } else {
+            const int lim = vis - 4 * h;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
-                s[mt] = mfma32(lds16(&sm.k[(32 * mt + j) * KST + 16 * ks + 8 * h]), qb[ks], s[mt]);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int d = lim - (32 * mt + 8 * (e >> 2) + (e & 3));
+                    s[mt][e] = __uint_as_float((uint32_t)(d >> 31) & 0xff800000u);
+                }
+            qk();
+        }
 
         __builtin_amdgcn_s_setprio(0);
         // the next tile's query rows (into the registers just consumed) and metadata
@@ -198,24 +230,12 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
             ent_next = entry_of(t + 2);
         }
 
-        // softmax over the block: element 4 q + r of s[mt] is token 32 mt + 8 q + 4 h + r
-        const int vis = meta.valid ? meta.pos - meta.blk * kBlk : -1;
+        // softmax over the block (masked scores are -inf)
         float mx = -INFINITY;
-        if (__builtin_amdgcn_readfirstlane(__all(vis >= kBlk - 1))) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int tok = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-                    s[mt][e] = (tok <= vis) ? s[mt][e] : -INFINITY;
-                    mx = fmaxf(mx, s[mt][e]);
-                }
-        }
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
         mx = wave_max_xor(mx, 32);
         const float off = (mx == -INFINITY) ? 0.f : -mx * scale_log2;
         float l = 0.f;
