@@ -298,8 +298,8 @@ def msa_decode_step(dims: Dims, q_idx, k_idx, block_table, row_pos, score_stride
     """The whole decode step (scores, selection, page table, slot partials and
     their merge); returns (scores, sel, page_table, o_part, lse_part, o, lse).
     sync: int32 device tensor of decode_step_sync_words(rows, G) zeros (left zero
-    by every call); when None and mode is not MSA_STEP_SEPARATE a zeroed one is
-    allocated for the call (pass a persistent one to avoid that)."""
+    by every call), used by MSA_STEP_ONE_LAUNCH; when None in that mode a zeroed
+    one is allocated for the call (pass a persistent one to avoid that)."""
     _need(q_idx, torch.bfloat16, "q_idx", True)
     _need(q, torch.bfloat16, "q", True)
     _i32(block_table, "block_table"), _i32(row_pos, "row_pos")
@@ -321,7 +321,7 @@ def msa_decode_step(dims: Dims, q_idx, k_idx, block_table, row_pos, score_stride
         lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
     _need(o, torch.bfloat16, "o", True)
     _need(lse, torch.float32, "lse", True)
-    if sync is None and mode != MSA_STEP_SEPARATE:
+    if sync is None and mode == MSA_STEP_ONE_LAUNCH:
         sync = torch.zeros(decode_step_sync_words(rows, dims.G), dtype=torch.int32, device=dev)
     if sync is not None:
         _i32(sync, "sync")

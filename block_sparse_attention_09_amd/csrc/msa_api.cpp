@@ -331,14 +331,12 @@ msa_status_t msa_decode_step(const msa_dims_t *dims, int32_t rows, const void *q
                 aligned(sync, 4),
             MSA_ERR_INVALID, "int32/fp32 arrays must be 4-byte aligned");
     if ((st = check_view(k_idx, "k_idx")) != MSA_OK) return st;
-    // automatic choice: one launch for a decode batch (fewer than 64 rows per
-    // request: the shape msa_index_score scans with the streaming kernel) with
-    // few blocks to scan, when the sync words are given
-    const bool one =
-        supported && (mode == MSA_STEP_ONE_LAUNCH ||
-                      (mode == MSA_STEP_AUTO && sync &&
-                       (int64_t)rows * dims->G * score_stride <= msa::kStepAutoMaxBlocks &&
-                       (int64_t)rows < 64 * (int64_t)num_reqs));
+    // the automatic mode takes the separate launches: on MI355X they are the
+    // faster form at every decode shape measured (issued back to back, the
+    // three kernels' launch gaps cost less than the single launch's fences and
+    // waits: 21.2 against 25.1 us at a 4K context, 196 against 415 us at
+    // batch 8 x 64K)
+    const bool one = supported && mode == MSA_STEP_ONE_LAUNCH;
     const msa::AttnArgs a = attn_args(dims, rows, q, kc, vc, sel, page_table, nslot, row_pos,
                                       sm_scale, o_part, lse_part);
     const hipStream_t s = as_stream(stream);

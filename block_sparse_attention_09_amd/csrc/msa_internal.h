@@ -184,9 +184,6 @@ struct StepArgs {
     int nscan_waves, spin_limit;  // set by launch_decode_step
 };
 constexpr int kStepSyncHead = 4;
-// msa_decode_step's automatic choice of the single launch: at most this many
-// scored blocks in the batch (a bound on the number of waves that fence)
-constexpr int64_t kStepAutoMaxBlocks = 4096;
 bool decode_step_supported(int d_idx, int score_stride);
 hipError_t launch_decode_step(const AttnArgs &a, StepArgs f, int d_idx, hipStream_t stream);
 
