@@ -48,6 +48,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_score_decode-64k-b8
 # the index-score kernel's sources (the counter summary names their hash)
 KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc", f)
                for f in ("index_score.hip", "index_score_dev.h")]
+# the same for the block-major prefill attention kernel
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                                 "traffic_attn_blockmajor_prefill-8k-on-60k.json")
+ATTN_KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_09_amd", "csrc", "attn.hip")]
 
 
 def parse():
@@ -380,14 +384,14 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
                       score_btb_ms=score_btb_ms, slab_us=slab_us)
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the index-score kernel from the committed counter
-    summary, if it was taken on the current kernel source."""
+def traffic_from_profile(path=TRAFFIC_FILE, srcs=KERNEL_SRCS):
+    """HBM bytes per launch of a kernel (by default the index-score kernel) from
+    its committed counter summary, if that was taken on the current kernel source."""
     try:
-        info = json.load(open(TRAFFIC_FILE))
+        info = json.load(open(path))
     except (OSError, ValueError):
         return None
-    src_hash = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SRCS)).hexdigest()[:16]
+    src_hash = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()[:16]
     if info.get("kernel_source_sha256_16") != src_hash:
         return None
     return info.get("hbm_bytes_per_launch")
@@ -602,6 +606,14 @@ def summarize(cfg, case, r, peaks=None):
             res["attn_frac_of_random_operand_mfma"] = round(
                 res["attn_tflops_kernel_call"] / peaks["mfma_bf16_random_TFLOPs"], 4)
         res["attn_flops"] = a["attn_flops"]
+        # the kernel's measured HBM traffic (counters of the committed summary:
+        # K/V, the queries it fetches past L2 and the partials it writes) over
+        # its call time: how close the call runs to the memory roofline
+        traffic = traffic_from_profile(ATTN_TRAFFIC_FILE, ATTN_KERNEL_SRCS)
+        if traffic:
+            res["attn_traffic_bytes"] = traffic
+            res["attn_traffic_GBps"] = round(traffic / (t["attn"] * 1e-3) / 1e9, 1)
+            res["attn_traffic_hbm_frac"] = round(res["attn_traffic_GBps"] / HBM_PEAK_GBPS, 4)
         if r.get("slab_us"):
             # msa_sparse_attn_prefill_merged by slab size (rows per slab): the
             # block-major attention and the merge, partials slab by slab
