@@ -69,6 +69,9 @@ def parse():
                          "many MiB (reference for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
     ap.add_argument("--eager-only", action="store_true",
                     help="time the eager step only (no graph capture), for counter runs")
+    ap.add_argument("--no-slab-sweep", action="store_true",
+                    help="skip the prefill slab-size sweep (so that a kernel trace holds only "
+                         "the full-batch attention launches)")
     return ap.parse_args()
 
 
@@ -97,7 +100,7 @@ def algorithmic(case, sel=None):
     return out
 
 
-def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
+def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False, slab_sweep=True):
     import torch
     import block_sparse_attention_09_amd as msa
     import msa_synth
@@ -268,7 +271,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False):
     # (msa_sparse_attn_prefill_merged), each slab's partials merged right after
     # its pass, against the whole batch as one slab.  Same output bit for bit.
     slab_us = None
-    if case.prefill:
+    if case.prefill and slab_sweep:
         slab_us = {}
         for div in (1, 2, 4, 8, 16, 32):
             slab = max(1, case.rows // div)
@@ -666,7 +669,8 @@ def main():
     for cfg in order:
         steps = args.steps if cfg == main_cfg else max(5, min(args.steps, 20))
         print(f"[bench] workload {cfg}: {steps} steps", file=sys.stderr, flush=True)
-        case, r = run_workload(cfg, steps, args.warmup, graph_replay=not args.eager_only)
+        case, r = run_workload(cfg, steps, args.warmup, graph_replay=not args.eager_only,
+                               slab_sweep=not args.no_slab_sweep)
         results[cfg] = summarize(cfg, case, r, peaks)
         if not args.no_cpu_baseline:
             # the oracle on the host cores, same inputs, after the GPU timing
