@@ -53,12 +53,10 @@ struct AttnSmem {
     bf16_t vt[128 * KST];   // V page, [dim][permuted token position]
 };
 
-// LDS column of token t in V^T.  In every 16-token PV step the MFMA K index
-// k = 8 h + 4 q + r holds token 8 q + 4 h + r of the step, which is where the
-// S^T accumulators leave P in lane half h: swap bits 2 and 3 of t.
-__device__ __forceinline__ int vt_col(int t) {
-    return (t & ~15) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2) | (t & 3);
-}
+// Column order of V^T in LDS: token t sits in column t with bits 2 and 3
+// swapped.  In every 16-token PV step the MFMA K index k = 8 h + 4 q + r holds
+// token 8 q + 4 h + r of the step, which is where the S^T accumulators leave P
+// in lane half h.
 
 __device__ __forceinline__ bf16x8 lds16(const bf16_t *p) {
     return as_bf16x8(*reinterpret_cast<const u32x4 *>(p));
@@ -87,22 +85,51 @@ __device__ __forceinline__ void stage_kv_load(KvStage &st, const bf16_t *kp, int
 // query of the unit, possibly never written) are stored as zeros: a zero
 // softmax weight times a non-finite V value would still poison P V, and the
 // masked scores start from -inf (blockmajor_wave), which a non-finite K row
-// would turn into NaN.
+// would turn into NaN.  V is transposed in LDS: written row-major into the V^T
+// area with whole-row 16-byte stores, read back column-wise with the gfx950
+// transposing LDS read (each lane of a 16-lane group receives one dimension
+// of four consecutive tokens), then written as V^T rows, again 16 bytes per
+// lane: no element-wise scatter.  Holds two workgroup barriers.
 __device__ __forceinline__ void stage_kv_store(AttnSmem &sm, const KvStage &st, int last_tok) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = tid + kAttnThreads * i;
         const int t = c >> 4, d0 = (c & 15) * 8;
-        *reinterpret_cast<u32x4 *>(&sm.k[t * KST + d0]) =
-            (t <= last_tok) ? st.kw[i] : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 v = (t <= last_tok) ? st.vw[i] : u32x4{0u, 0u, 0u, 0u};
-        bf16_t *col = &sm.vt[d0 * KST + vt_col(t)];
+        const u32x4 zero{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(&sm.k[t * KST + d0]) = (t <= last_tok) ? st.kw[i] : zero;
+        *reinterpret_cast<u32x4 *>(&sm.vt[t * KST + d0]) = (t <= last_tok) ? st.vw[i] : zero;
+    }
+    __syncthreads();
+    // Piece (dimension block D0 = 16 (pg % 8), column group j = pg / 8) of V^T:
+    // rows D0 .. D0 + 15, columns 8 j .. 8 j + 7, which hold tokens T0 .. T0 + 3
+    // and T0 + 8 .. T0 + 11 with T0 = 16 (j / 2) + 4 (j % 2) (the column
+    // order above: columns 8 j .. 8 j + 3 are tokens T0 .. T0 + 3).  Group c
+    // of wave w takes pieces pg = 16 it + 4 w + c; lane s of the group points
+    // the transposing read at token T0 + s / 4, dims D0 + 4 (s % 4), and
+    // receives dimension D0 + s of the four tokens.
+    const int grp = tid >> 4, s16 = tid & 15;
+    v4i16 lo[8], hi[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            col[(2 * e) * KST] = (bf16_t)(v[e] & 0xffffu);
-            col[(2 * e + 1) * KST] = (bf16_t)(v[e] >> 16);
-        }
+    for (int it = 0; it < 8; ++it) {
+        const int pg = 16 * it + grp;
+        const int D0 = 16 * (pg & 7), j = pg >> 3;
+        const int T0 = 16 * (j >> 1) + 4 * (j & 1);
+        const bf16_t *src = &sm.vt[(T0 + (s16 >> 2)) * KST + D0 + 4 * (s16 & 3)];
+        lo[it] = lds_read_tr(reinterpret_cast<const char *>(src));
+        hi[it] = lds_read_tr(reinterpret_cast<const char *>(src + 8 * KST));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int pg = 16 * it + grp;
+        const int D0 = 16 * (pg & 7), j = pg >> 3;
+        u32x4 w;
+        w[0] = (uint32_t)(uint16_t)lo[it][0] | ((uint32_t)(uint16_t)lo[it][1] << 16);
+        w[1] = (uint32_t)(uint16_t)lo[it][2] | ((uint32_t)(uint16_t)lo[it][3] << 16);
+        w[2] = (uint32_t)(uint16_t)hi[it][0] | ((uint32_t)(uint16_t)hi[it][1] << 16);
+        w[3] = (uint32_t)(uint16_t)hi[it][2] | ((uint32_t)(uint16_t)hi[it][3] << 16);
+        *reinterpret_cast<u32x4 *>(&sm.vt[(D0 + s16) * KST + 8 * j]) = w;
     }
 }
 
