@@ -22,7 +22,7 @@
 //   O^T = V^T P^T  V^T from LDS in the token order that matches where the S^T
 //                  accumulators leave P, P^T repacked to bf16 in registers
 // and writes the normalised partial (bf16) and its natural-log LSE (fp32).
-// A wave needs about 250 registers, so two workgroups (eight waves) share a CU
+// A workgroup holds 78 KB of LDS, so two workgroups (eight waves) share a CU
 // and one wave's softmax overlaps another's matrix-core work.  The units' query
 // lists come from a counting-sort inversion of the selection built in the
 // caller's workspace.
