@@ -198,6 +198,44 @@ def test_prefill_shapes(name):
     pu.check_output(res["o"], res["lse"], o, lse)
 
 
+def _random_shape(i):
+    """Seeded draw of one small case: groups, heads, index vectors and dims, k,
+    request count and context lengths (partial blocks included), paging, lower
+    bounds, poisoned tails, decode or prefill rows."""
+    rng = np.random.default_rng(7000 + i)
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    Hg = int(rng.choice([h for h in (1, 2, 4, 8, 16) if G * h <= 64]))
+    kw = dict(seed=7000 + i, G=G, Hg=Hg, d_idx=int(rng.choice([64, 128])),
+              n_idx=int(rng.choice([1, 2, 4, 5, 8])), k=int(rng.choice([0, 1, 2, 3, 5, 8, 13, 21])),
+              paged=bool(rng.integers(0, 2)), lo_frac=float(rng.choice([0.0, 0.4])),
+              poison=["nan", True][int(rng.integers(0, 2))])
+    if i % 2:
+        reqs = int(rng.integers(1, 3))
+        ctx = [int(rng.integers(200, 3000)) for _ in range(reqs)]
+        kw.update(ctx_lens=ctx, prefill_rows=[int(rng.integers(1, min(c, 300 // reqs) + 1))
+                                              for c in ctx])
+    else:
+        reqs = int(rng.integers(1, 7))
+        kw.update(ctx_lens=[int(rng.integers(1, 5000)) for _ in range(reqs)])
+    return kw
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_shapes(i):
+    """Thirty-two seeded random small cases, decode (even i) and prefill (odd i), the
+    whole path against the oracle: scores, selection, page table, partials and
+    merged output."""
+    kw = _random_shape(i)
+    print(f"[case] random shape {i}: {kw}", flush=True)
+    case = _build(**kw)
+    res = pu.gpu_path(case)
+    rows = list(range(case.rows))
+    _full_compare(case, res, rows)
+    op, lp, o, lse = pu.oracle_attn(case, rows, res["sel"].numpy(), res["pt"].numpy())
+    pu.check_partials(res["o_part"], res["lse_part"], op, lp)
+    pu.check_output(res["o"], res["lse"], o, lse)
+
+
 def test_prefill_several_requests():
     """Rows of three requests in one call: row tiles that straddle requests,
     request-specific pages and positions, through the tiled scorer and the
