@@ -387,12 +387,15 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False, slab_s
                       score_btb_ms=score_btb_ms, slab_us=slab_us)
 
 
-def traffic_from_profile(path=TRAFFIC_FILE, srcs=KERNEL_SRCS):
+def traffic_from_profile(workload, path=TRAFFIC_FILE, srcs=KERNEL_SRCS):
     """HBM bytes per launch of a kernel (by default the index-score kernel) from
-    its committed counter summary, if that was taken on the current kernel source."""
+    its committed counter summary, if that was taken on this workload and on the
+    current kernel source."""
     try:
         info = json.load(open(path))
     except (OSError, ValueError):
+        return None
+    if info.get("workload") != workload:
         return None
     src_hash = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()[:16]
     if info.get("kernel_source_sha256_16") != src_hash:
@@ -612,7 +615,7 @@ def summarize(cfg, case, r, peaks=None):
         # the kernel's measured HBM traffic (counters of the committed summary:
         # K/V, the queries it fetches past L2 and the partials it writes) over
         # its call time: how close the call runs to the memory roofline
-        traffic = traffic_from_profile(ATTN_TRAFFIC_FILE, ATTN_KERNEL_SRCS)
+        traffic = traffic_from_profile(case.name, ATTN_TRAFFIC_FILE, ATTN_KERNEL_SRCS)
         if traffic:
             res["attn_traffic_bytes"] = traffic
             res["attn_traffic_GBps"] = round(traffic / (t["attn"] * 1e-3) / 1e9, 1)
@@ -714,13 +717,27 @@ def main():
     a = main_run["alg"]
     t_score = main_run["per_call_ms"]["index_score"]
     achieved = a["score_bytes"] / (t_score * 1e-3) / 1e9
-    roofline = dict(kernel="index_score_stream_kernel", bound="hbm", achieved=round(achieved, 1),
-                    peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
-                    traffic=traffic_from_profile(), alg_bytes_per_launch=a["score_bytes"],
-                    avg_launch_us=round(t_score * 1e3, 2),
-                    frac_of_measured_read=round(achieved / peaks["stream_read_GBps"], 4))
+    if main_case.prefill:
+        # a prefill headline: the block-major attention kernel against the bf16
+        # matrix-core peak (traffic: its HBM bytes from the committed counters)
+        t_attn = main_run["per_call_ms"]["attn"]
+        tf = a["attn_flops"] / (t_attn * 1e-3) / 1e12
+        roofline = dict(kernel="attn_blockmajor_kernel", bound="mfma", achieved=round(tf, 2),
+                        peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                        traffic=traffic_from_profile(main_case.name, ATTN_TRAFFIC_FILE,
+                                                     ATTN_KERNEL_SRCS),
+                        alg_flops_per_launch=a["attn_flops"], avg_launch_us=round(t_attn * 1e3, 2),
+                        frac_of_random_operand_mfma=round(tf / peaks["mfma_bf16_random_TFLOPs"], 4))
+    else:
+        roofline = dict(kernel="index_score_stream_kernel", bound="hbm",
+                        achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBPS, 4),
+                        traffic=traffic_from_profile(main_case.name),
+                        alg_bytes_per_launch=a["score_bytes"],
+                        avg_launch_us=round(t_score * 1e3, 2),
+                        frac_of_measured_read=round(achieved / peaks["stream_read_GBps"], 4))
     btb = main_run.get("score_btb_ms")
-    if btb:
+    if btb and not main_case.prefill:
         # the same kernel timed back to back (see run_workload): its own duration,
         # without the dispatch latency each per-launch event pair also holds
         roofline["back_to_back_us"] = round(btb * 1e3, 2)
