@@ -302,6 +302,45 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False, slab_s
             slab_us[str(slab)] = round(min(ts), 1)
             del wsm, om, lm
         torch.cuda.empty_cache()
+    # Prefill: the block-major kernel's memory pattern without its arithmetic
+    # (msa_peak_row_copy): every (row, group, slot) entry's Hg query rows loaded
+    # and its Hg partial rows stored, in the order of the kernel's (group, page)
+    # units, 32-row tiles, about one unit of tiles per workgroup; queries loaded
+    # in the matrix-core operand layout as the kernel loads them, and as whole
+    # rows.  Written into o_part, which the next step overwrites.
+    pattern = None
+    if case.prefill:
+        r_i, g_i, s_i = (sel >= 0).nonzero(as_tuple=True)
+        order = torch.argsort(pt[r_i, g_i, s_i].long() * case.G + g_i, stable=True)
+        r_i, g_i, s_i = r_i[order], g_i[order], s_i[order]
+        hh = torch.arange(case.Hg, device=dev)
+        qrow = r_i[:, None] * case.H + g_i[:, None] * case.Hg + hh[None, :]
+        prow = (qrow * case.nslot + s_i[:, None]).reshape(-1)
+        qrow = qrow.reshape(-1)
+        n = qrow.numel() // 32 * 32
+        l_idx, s_idx = qrow[:n].to(torch.int32).contiguous(), prow[:n].to(torch.int32).contiguous()
+        tiles = n // 32
+        tpw = max(1, min(64, round(tiles / max(1, int(torch.unique(pt[r_i, g_i, s_i].long() * case.G
+                                                                    + g_i).numel())))))
+        pattern = dict(rows=n, bytes_each_way=n * 256, tiles_per_workgroup=tpw)
+        for layout, key in ((1, "operand_layout_us"), (0, "whole_rows_us")):
+            def run_pattern():
+                msa.msa_peak_row_copy(case.q, o_part, l_idx, s_idx, tiles_per_wg=tpw,
+                                      load_layout=layout)
+            run_pattern()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run_pattern()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            pattern[key] = round(min(ts), 1)
+        del l_idx, s_idx, qrow, prow, r_i, g_i, s_i, order
     per_fused = None
     if fused:
         for _ in range(warmup):
@@ -337,7 +376,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False, slab_s
         return case, dict(total_ms=eager_ms, ms_per_step=eager_ms / steps, eager_ms=eager_ms,
                           eager_ms_per_step=eager_ms / steps, wall_s=wall, per_call_ms=per,
                           per_call_fused_ms=per_fused, step_pct_ms=pct, alg=alg, sel=sel.cpu(),
-                          score_btb_ms=score_btb_ms, slab_us=slab_us)
+                          score_btb_ms=score_btb_ms, slab_us=slab_us, pattern=pattern)
 
     # The same step captured once in a HIP graph and replayed: removes the
     # host launch gaps between the calls.  Every replay must reproduce the
@@ -384,7 +423,7 @@ def run_workload(cfg, steps, warmup, graph_replay=True, kv_on_host=False, slab_s
                       eager_ms_per_step=eager_ms / steps, graph_ms_per_step=graph_ms / steps,
                       wall_s=wall, per_call_ms=per, per_call_fused_ms=per_fused,
                       step_pct_ms=pct, alg=alg, sel=sel.cpu(), warm_ms_per_step=warm_ms / steps,
-                      score_btb_ms=score_btb_ms, slab_us=slab_us)
+                      score_btb_ms=score_btb_ms, slab_us=slab_us, pattern=pattern)
 
 
 def traffic_from_profile(workload, path=TRAFFIC_FILE, srcs=KERNEL_SRCS):
@@ -620,6 +659,9 @@ def summarize(cfg, case, r, peaks=None):
             res["attn_traffic_bytes"] = traffic
             res["attn_traffic_GBps"] = round(traffic / (t["attn"] * 1e-3) / 1e9, 1)
             res["attn_traffic_hbm_frac"] = round(res["attn_traffic_GBps"] / HBM_PEAK_GBPS, 4)
+        if r.get("pattern"):
+            # the kernel's query loads and partial stores alone (msa_peak_row_copy)
+            res["attn_memory_pattern"] = r["pattern"]
         if r.get("slab_us"):
             # msa_sparse_attn_prefill_merged by slab size (rows per slab): the
             # block-major attention and the merge, partials slab by slab

@@ -18,7 +18,8 @@ Helper: empty_lse_part (partial LSEs in the C ABI's [rows][nslot][H] layout);
 MSA_STEP_AUTO, MSA_STEP_ONE_LAUNCH, MSA_STEP_SEPARATE (msa_decode_step modes),
 decode_step_sync_words (length of its int32 sync array)
 Measured-peak probes (``include/msa_peaks.h``, not steps of the path):
-    msa_peak_stream_read, msa_peak_stream_write, msa_peak_mfma_bf16, msa_peak_mfma_bf16_random
+    msa_peak_stream_read, msa_peak_stream_write, msa_peak_row_copy, msa_peak_mfma_bf16,
+    msa_peak_mfma_bf16_random
 """
 from .binding import (  # noqa: F401
     MSA_STEP_AUTO,
@@ -38,6 +39,7 @@ from .binding import (  # noqa: F401
     msa_lse_merge,
     msa_peak_mfma_bf16,
     msa_peak_mfma_bf16_random,
+    msa_peak_row_copy,
     msa_peak_stream_read,
     msa_peak_stream_write,
     msa_prefill_merged_workspace_size,

@@ -66,6 +66,7 @@ _SIGS = {
     "msa_gather_pages": [_DIMS, _I32, _P, _I32, View, View, _P, _P, _P, _P],
     "msa_peak_stream_read": [_P, ctypes.c_size_t, _P, _P],
     "msa_peak_stream_write": [_P, ctypes.c_size_t, ctypes.c_uint32, _P],
+    "msa_peak_row_copy": [_P, _P, _P, _P, ctypes.c_int64, _I32, _I32, _P],
     "msa_peak_mfma_bf16": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
     "msa_peak_mfma_bf16_random": [_I32, _P, ctypes.POINTER(ctypes.c_double), _P],
 }
@@ -476,6 +477,24 @@ def msa_peak_stream_write(buf: torch.Tensor, tag: int = 0, stream=None):
     _check(load().msa_peak_stream_write(_ptr(buf), buf.numel() * buf.element_size(),
                                         int(tag) & 0xffffffff, _stream(stream)),
            "msa_peak_stream_write")
+
+
+def msa_peak_row_copy(src: torch.Tensor, dst: torch.Tensor, load_idx: torch.Tensor,
+                      store_idx: torch.Tensor, tiles_per_wg: int = 64, load_layout: int = 1,
+                      stream=None):
+    """Launch the row gather-scatter probe (include/msa_peaks.h): destination row
+    store_idx[i] of dst gets source row load_idx[i] of src, rows of 256 bytes."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if (t.numel() * t.element_size()) % 256:
+            raise ValueError(f"{name} must hold whole 256-byte rows")
+    _i32(load_idx, "load_idx"), _i32(store_idx, "store_idx")
+    if load_idx.numel() != store_idx.numel():
+        raise ValueError("load_idx and store_idx must have the same length")
+    _check(load().msa_peak_row_copy(_ptr(src), _ptr(dst), _ptr(load_idx), _ptr(store_idx),
+                                    ctypes.c_int64(load_idx.numel()), int(tiles_per_wg),
+                                    int(load_layout), _stream(stream)), "msa_peak_row_copy")
 
 
 def msa_peak_mfma_bf16(iters: int, sink: torch.Tensor, stream=None) -> float:

@@ -567,6 +567,26 @@ msa_status_t msa_peak_stream_write(void *buf, size_t bytes, uint32_t tag, msa_st
                       "msa_peak_stream_write");
 }
 
+msa_status_t msa_peak_row_copy(const void *src, void *dst, const int32_t *load_idx,
+                               const int32_t *store_idx, int64_t n, int32_t tiles_per_wg,
+                               int32_t load_layout, msa_stream_t stream) {
+    REQUIRE(n >= 0 && n % 32 == 0, MSA_ERR_INVALID, "n = %lld must be a multiple of 32 (>= 0)",
+            (long long)n);
+    REQUIRE(tiles_per_wg >= 1 && tiles_per_wg <= 64, MSA_ERR_INVALID,
+            "tiles_per_wg = %d must be in [1, 64]", tiles_per_wg);
+    REQUIRE(load_layout == 0 || load_layout == 1, MSA_ERR_INVALID,
+            "load_layout = %d must be 0 or 1", load_layout);
+    REQUIRE(n / 32 / tiles_per_wg < ((int64_t)1 << 31), MSA_ERR_INVALID, "n too large");
+    if (n == 0) return ok();
+    REQUIRE(src && dst && load_idx && store_idx, MSA_ERR_NULL,
+            "src, dst, load_idx and store_idx are required");
+    REQUIRE(aligned(src, 16) && aligned(dst, 16) && aligned(load_idx, 4) && aligned(store_idx, 4),
+            MSA_ERR_INVALID, "src and dst must be 16-byte aligned, the indices 4-byte aligned");
+    return hip_status(msa::launch_peak_row_copy(src, dst, load_idx, store_idx, n, tiles_per_wg,
+                                                load_layout, as_stream(stream)),
+                      "msa_peak_row_copy");
+}
+
 msa_status_t msa_peak_mfma_bf16(int32_t iters, float *sink, double *flops, msa_stream_t stream) {
     REQUIRE(iters >= 1, MSA_ERR_INVALID, "iters = %d must be >= 1", iters);
     REQUIRE(sink && flops, MSA_ERR_NULL, "sink and flops are required");

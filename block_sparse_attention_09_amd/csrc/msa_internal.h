@@ -209,6 +209,9 @@ hipError_t launch_gather_pages(int rows, int G, int nslot, const int32_t *page_t
 hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
                                    hipStream_t stream);
 hipError_t launch_peak_stream_write(void *buf, int64_t bytes, uint32_t tag, hipStream_t stream);
+hipError_t launch_peak_row_copy(const void *src, void *dst, const int32_t *load_idx,
+                                const int32_t *store_idx, int64_t n, int tiles_per_wg,
+                                int layout, hipStream_t stream);
 hipError_t launch_peak_mfma_bf16(int iters, float *sink, double *flops, hipStream_t stream);
 hipError_t launch_peak_mfma_bf16_random(int iters, float *sink, double *flops,
                                        hipStream_t stream);

@@ -123,7 +123,88 @@ __global__ __launch_bounds__(kPeakThreads) void mfma_random_loop_kernel(int iter
     if (s == 1.2345f) sink[0] = s;
 }
 
+// Row gather-scatter: the memory pattern of the block-major prefill kernel
+// without its arithmetic.  A workgroup takes `tpw` consecutive tiles of 32
+// rows of 256 bytes, its four waves one tile each in turn; a wave loads its
+// tile's 32 source rows (cached loads: four whole rows per instruction, or 32
+// rows x 32 bytes per instruction, the layout of 32 MFMA operand rows), passes
+// them through its own LDS stage (rows padded by 16 bytes) and stores four
+// whole rows per instruction to the destination rows, non-temporally.  The
+// next tile's loads are issued before the current tile's stores; the row
+// indices of all of a wave's tiles are loaded up front (at most 16 tiles per
+// wave), so no wait for a row index has to wait for earlier stores.
+constexpr int kCopyMaxTilesPerWg = 64;
+constexpr int kCopyStageRow = 17;  // 16-B chunks per staged row (16 + 1 pad)
+
+__global__ __launch_bounds__(kPeakThreads) void row_copy_kernel(
+    const bf16_t *__restrict__ src, bf16_t *__restrict__ dst, const int32_t *__restrict__ lidx,
+    const int32_t *__restrict__ sidx, int64_t ntiles, int tpw, int layout) {
+    __shared__ u32x4 stage[kPeakThreads / kWave][32 * kCopyStageRow];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * tpw;
+    const int64_t t1 = t0 + tpw < ntiles ? t0 + tpw : ntiles;
+    const int nmine = t0 + w < t1 ? (int)((t1 - t0 - w + 3) / 4) : 0;  // <= 16
+    if (nmine == 0) return;
+    // row indices of this wave's tiles k = 0 .. nmine - 1 (tile t0 + w + 4 k):
+    // lane l holds row l % 32 of each
+    int li[kCopyMaxTilesPerWg / 4], si[kCopyMaxTilesPerWg / 4];
+#pragma unroll
+    for (int k = 0; k < kCopyMaxTilesPerWg / 4; ++k) {
+        const int64_t e = (t0 + w + 4 * k) * 32 + (lane & 31);
+        li[k] = k < nmine ? lidx[e] : 0;
+        si[k] = k < nmine ? sidx[e] : 0;
+    }
+    u32x4 *st = &stage[w][0];
+    auto load_tile = [&](int row_here, u32x4 (&v)[8]) {
+        if (layout == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = __shfl(row_here, 4 * i + (lane >> 4), kWave);
+                v[i] = ld16(src + (int64_t)row * 128 + 8 * (lane & 15));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = ld16(src + (int64_t)row_here * 128 + 16 * i + 8 * (lane >> 5));
+        }
+    };
+    u32x4 v[8];
+    load_tile(li[0], v);
+#pragma unroll
+    for (int k = 0; k < kCopyMaxTilesPerWg / 4; ++k) {
+        if (k >= nmine) continue;  // wave-uniform
+        // stage row r of the tile at st[r * kCopyStageRow + chunk]
+        if (layout == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st[(4 * i + (lane >> 4)) * kCopyStageRow + (lane & 15)] = v[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st[(lane & 31) * kCopyStageRow + 2 * i + (lane >> 5)] = v[i];
+        }
+        if (k + 1 < kCopyMaxTilesPerWg / 4 && k + 1 < nmine) load_tile(li[k + 1], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int row = __shfl(si[k], r, kWave);
+            __builtin_nontemporal_store(st[r * kCopyStageRow + (lane & 15)],
+                                        reinterpret_cast<u32x4 *>(dst + (int64_t)row * 128 +
+                                                                  8 * (lane & 15)));
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_peak_row_copy(const void *src, void *dst, const int32_t *load_idx,
+                                const int32_t *store_idx, int64_t n, int tiles_per_wg,
+                                int layout, hipStream_t stream) {
+    const int64_t ntiles = n / 32;
+    const int64_t grid = (ntiles + tiles_per_wg - 1) / tiles_per_wg;
+    hipLaunchKernelGGL(row_copy_kernel, dim3((unsigned)grid), dim3(kPeakThreads), 0, stream,
+                       static_cast<const bf16_t *>(src), static_cast<bf16_t *>(dst), load_idx,
+                       store_idx, ntiles, tiles_per_wg, layout);
+    return hipGetLastError();
+}
 
 hipError_t launch_peak_stream_read(const void *buf, int64_t bytes, float *sink,
                                    hipStream_t stream) {

@@ -36,6 +36,28 @@ msa_status_t msa_peak_stream_read(const void *buf, size_t bytes, float *sink,
  * Errors: MSA_ERR_INVALID (alignment, size), MSA_ERR_NULL, MSA_ERR_HIP. */
 msa_status_t msa_peak_stream_write(void *buf, size_t bytes, uint32_t tag, msa_stream_t stream);
 
+/* Row gather-scatter: for i < n, destination row store_idx[i] receives source
+ * row load_idx[i], rows of 256 bytes (device pointers; src and dst 16-byte
+ * aligned).  This is the memory pattern of the KV-block-major prefill kernel
+ * (msa_sparse_attn_prefill) without its arithmetic: with load_idx the query
+ * rows of the (row, head) pairs in the order the kernel's units take them and
+ * store_idx their partial rows, its time is what the kernel's query loads and
+ * partial stores cost by themselves.  The rows go in tiles of 32; each
+ * 256-thread workgroup takes tiles_per_wg (1..64) consecutive tiles, its four
+ * waves one tile each in turn.  load_layout 0 loads four whole rows per
+ * instruction (16 bytes per lane), 1 loads 32 rows x 32 bytes per instruction
+ * (the layout of 32 matrix-core operand rows, as the kernel loads queries);
+ * either way a wave passes its 32 rows through LDS and stores four whole rows
+ * per instruction, non-temporally, and issues the next tile's loads before the
+ * current tile's stores.  n is a multiple of 32.  Preconditions (device data,
+ * not checked): every load_idx names a source row, every store_idx a
+ * destination row; with distinct store_idx the destination rows are an exact
+ * copy.  Errors: MSA_ERR_INVALID (n, tiles_per_wg, load_layout, alignment),
+ * MSA_ERR_NULL, MSA_ERR_HIP. */
+msa_status_t msa_peak_row_copy(const void *src, void *dst, const int32_t *load_idx,
+                               const int32_t *store_idx, int64_t n, int32_t tiles_per_wg,
+                               int32_t load_layout, msa_stream_t stream);
+
 /* Register-resident bf16 matrix-core loop: two 256-thread workgroups per CU,
  * each wave runs `iters` iterations of four independent 32x32x16 bf16 MFMA
  * accumulation chains.  *flops (host) receives the floating-point operations the

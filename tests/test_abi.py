@@ -294,6 +294,16 @@ def test_peak_probe_validation(lib):
     assert lib.msa_peak_stream_write(None, 0, 0, None) == MSA_OK
     assert lib.msa_peak_mfma_bf16_random(0, FAKE, ctypes.byref(flops), None) == MSA_ERR_INVALID
     assert lib.msa_peak_mfma_bf16_random(8, None, ctypes.byref(flops), None) == MSA_ERR_NULL
+    # row gather-scatter: every call below fails validation (or has n = 0) before any launch
+    assert lib.msa_peak_row_copy(FAKE, FAKE, FAKE, FAKE, 33, 64, 0, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_row_copy(FAKE, FAKE, FAKE, FAKE, -32, 64, 0, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_row_copy(FAKE, FAKE, FAKE, FAKE, 64, 0, 0, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_row_copy(FAKE, FAKE, FAKE, FAKE, 64, 65, 1, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_row_copy(FAKE, FAKE, FAKE, FAKE, 64, 64, 2, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_row_copy(None, FAKE, FAKE, FAKE, 64, 64, 0, None) == MSA_ERR_NULL
+    assert lib.msa_peak_row_copy(FAKE, FAKE, None, FAKE, 64, 64, 0, None) == MSA_ERR_NULL
+    assert lib.msa_peak_row_copy(MISALIGNED, FAKE, FAKE, FAKE, 64, 64, 0, None) == MSA_ERR_INVALID
+    assert lib.msa_peak_row_copy(None, None, None, None, 0, 64, 0, None) == MSA_OK
 
 
 def test_binding_refuses_host_tensors():

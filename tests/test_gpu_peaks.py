@@ -68,3 +68,23 @@ def test_random_operand_mfma_probe():
     ms = _time(lambda: msa.msa_peak_mfma_bf16_random(iters, sink))
     tflops = flops / (ms * 1e-3) / 1e12
     assert 200.0 < tflops < 2600.0, tflops
+
+
+@pytest.mark.parametrize("layout,tpw", [(0, 64), (1, 64), (1, 7), (0, 1)])
+def test_row_copy_probe(layout, tpw):
+    """Destination row store_idx[i] holds source row load_idx[i] exactly, every
+    other destination row is untouched; tile counts that leave ragged
+    workgroups (3,001 tiles over 64, 7 and 1 tiles per workgroup)."""
+    g = torch.Generator(device="cpu").manual_seed(11 + layout + tpw)
+    src_rows, dst_rows, n = 5000, 120_000, 32 * 3001
+    src = torch.randint(-2**31, 2**31 - 1, (src_rows, 64), generator=g, dtype=torch.int32)
+    load_idx = torch.randint(0, src_rows, (n,), generator=g, dtype=torch.int32)
+    store_idx = torch.randperm(dst_rows, generator=g)[:n].to(torch.int32)
+    dst = torch.full((dst_rows, 64), 7, dtype=torch.int32, device="cuda")
+    msa.msa_peak_row_copy(src.cuda(), dst, load_idx.cuda(), store_idx.cuda(), tiles_per_wg=tpw,
+                          load_layout=layout)
+    got = dst.cpu()
+    assert torch.equal(got[store_idx.long()], src[load_idx.long()])
+    untouched = torch.ones(dst_rows, dtype=torch.bool)
+    untouched[store_idx.long()] = False
+    assert bool(torch.all(got[untouched] == 7))
