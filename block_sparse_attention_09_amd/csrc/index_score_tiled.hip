@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256, 2) void index_score_tiled_kernel(
     int64_t kps, int64_t kgs, int64_t kts, const int32_t *__restrict__ block_table, int bt_stride,
     const int32_t *__restrict__ row_req, const int32_t *__restrict__ row_pos,
     const int32_t *__restrict__ blk_lo, float *__restrict__ scores, int score_stride, float scale) {
-    constexpr int KST = DIDX + 8;      // LDS row stride of a staged block (16-B pad)
+    constexpr int KST = DIDX + 16;     // LDS row stride of a staged block (32-B pad: conflict-free fragment reads)
     constexpr int NC = DIDX / 32;      // MFMA K chunks
     constexpr int LD_PER_THREAD = kBlk * DIDX / 8 / 256;   // 16-B loads per thread per block
     __shared__ __attribute__((aligned(16))) bf16_t kbuf[2][kBlk * KST];
