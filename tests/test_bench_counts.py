@@ -42,3 +42,24 @@ def test_multi_gpu_request_is_refused():
 def bench_root():
     import os
     return os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_profile_traffic_binds_to_workload_and_source(tmp_path):
+    """A committed counter summary is used only for the workload it was taken on
+    and only while the kernel sources hash to the recorded value."""
+    import hashlib
+    import json
+    import bench
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel source\n")
+    h = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    prof = tmp_path / "traffic.json"
+    prof.write_text(json.dumps({"workload": "decode-64k-b8", "kernel_source_sha256_16": h,
+                                "hbm_bytes_per_launch": 1234}))
+    assert bench.traffic_from_profile("decode-64k-b8", str(prof), [str(src)]) == 1234
+    assert bench.traffic_from_profile("decode-1m-b4", str(prof), [str(src)]) is None
+    src.write_text("// kernel source, changed\n")
+    assert bench.traffic_from_profile("decode-64k-b8", str(prof), [str(src)]) is None
+    assert bench.traffic_from_profile("decode-64k-b8", str(tmp_path / "missing.json"),
+                                      [str(src)]) is None
+
