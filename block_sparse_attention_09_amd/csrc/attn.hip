@@ -203,11 +203,6 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
         // barrier the compiler hoists all 64 fragment reads out of the loop
         // into registers and the wave no longer fits two per SIMD
         asm volatile("" ::: "memory");
-        // raised issue priority while this wave feeds the matrix cores (both
-        // MFMA sections below), so the other wave of the SIMD does its softmax,
-        // loads and stores in the gaps instead of delaying them (3 % on the 8K
-        // prefill chunk)
-        __builtin_amdgcn_s_setprio(1);
         // S^T = K Q^T: four 32-token row tiles, 8 dimension steps of 16.  The
         // causal mask lives in the accumulators' initial values: element 4 q + r
         // of s[mt] (token 32 mt + 8 q + 4 h + r) starts at 0 if the row sees the
@@ -247,7 +242,6 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
             qk();
         }
 
-        __builtin_amdgcn_s_setprio(0);
         // the next tile's query rows (into the registers just consumed) and metadata
         const bool more = t + 1 < my_tiles;
         TileMeta meta_next = meta;
@@ -284,7 +278,6 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
         }
         l = wave_sum_xor(l, 32);
 
-        __builtin_amdgcn_s_setprio(1);
         // O^T = V^T P^T: four 32-dim row tiles, 8 token steps of 16
         f32x16 o[4];
 #pragma unroll
@@ -295,7 +288,6 @@ __device__ __forceinline__ void blockmajor_wave(const AttnSmem &sm, bf16_t *osta
             for (int dt = 0; dt < 4; ++dt)
                 o[dt] = mfma32(lds16(&sm.vt[(32 * dt + j) * KST + 16 * ks + 8 * h]), pb[ks], o[dt]);
 
-        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) take_delivery(qb[ks]);
         take_delivery(meta_next.pos);
